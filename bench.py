@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the MFMA fragment-layout GEMM library on one MI355X.
+
+Headline workload: dense GEMM M = N = K = 4096, bf16 operands (A row-major,
+B column-major, leading dimension 4096 + 64 with NaN padding), fp32
+accumulation and fp32 output (ldc = 4096).  One step = one gemm_tile_mma call
+(global -> swizzled LDS -> MFMA with register accumulators -> one store per
+output element).  Operands are rounded to bf16 by the library before timing,
+as the workload specifies bf16 inputs.
+
+Prints ONE JSON line with the metric, a roofline object for the GEMM kernel
+(flops per launch / mean launch time from HIP events on the launch stream),
+the CPU oracle's throughput on the host cores, and per-workload figures for
+the other four workloads (single 256^3 GEMM, block-repeat tiles, split fp32
+GEMM with 1/2/3 chains, attention pair), each timed as 3 warm-up launches
+then the best of 3 rounds of 20 back-to-back launches.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def event_time_ms(fn, n, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end)
+
+
+def best_of(fn, stream, warm=3, rounds=3, per=20):
+    """Timing protocol of the Warp spike: 3 warm-up launches, then the best of
+    3 rounds of 20 back-to-back launches; returns ms per launch."""
+    for _ in range(warm):
+        fn()
+    return min(event_time_ms(fn, per, stream) for _ in range(rounds)) / per
+
+
+def cpu_baseline(a, bt):
+    """The oracle as it stands (numpy fp64 on the quantised inputs), timed on the
+    host's cores over the full 4096^3 problem."""
+    from oracle import reference as R
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"),
+                      default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    R.gemm_ref(a[:, :4096], bt[:, :4096], "bf16")
+    dt = time.perf_counter() - t0
+    return {"value": 2 * 4096 ** 3 / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "full 4096^3 bf16 GEMM: RNE quantisation of A and B plus the fp64 matmul, one run",
+            "seconds": round(dt, 3)}
+
+
+def extra_workloads(torch, mfl, inputs, stream):
+    dev = torch.device("cuda:0")
+    out = {}
+
+    def q16(x, dt):
+        src = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        o = torch.empty(src.shape, dtype=torch.int16, device=dev)
+        mfl.quantize_fp32(dt, src, o, src.numel(), stream)
+        return o
+
+    # single 256^3 fp16 GEMM (latency)
+    a, bt = inputs.gemm_small()
+    da, db = q16(a, mfl.F16), q16(bt, mfl.F16)
+    c = torch.empty((256, 256), device=dev)
+    ms = best_of(lambda: mfl.gemm_tile_mma(mfl.F16, 256, 256, 256, da, 256, 0, db, 256, 1, c, 256, 0, stream), stream)
+    out["gemm_256_f16"] = {"us": round(ms * 1e3, 2), "tflops": round(2 * 256 ** 3 / ms / 1e9, 2)}
+
+    # block repeat, 2048^2 output, 64 repeats
+    rep = {}
+    for tm, tn, tk, th in [(64, 64, 64, 64), (64, 64, 64, 128), (64, 64, 64, 256), (32, 32, 32, 128),
+                           (128, 128, 32, 128), (128, 128, 32, 256)]:
+        for name, dt in (("f16", mfl.F16), ("bf16", mfl.BF16)):
+            a, bt = inputs.block_repeat(tm, tn, tk)
+            da, db = q16(a, dt), q16(bt, dt)
+            c = torch.empty((2048, 2048), device=dev)
+            ms = best_of(lambda: mfl.gemm_block_repeat(dt, tm, tn, tk, th, 64, 2048, 2048, da, db, c, stream), stream)
+            rep[f"{tm}x{tn}x{tk}/{th}/{name}"] = round(2 * 2048 * 2048 * tk * 64 / ms / 1e9, 1)
+    out["block_repeat_tflops"] = rep
+
+    # split fp32 GEMM 4096^3, bf16 pieces
+    a, bt = inputs.gemm_split()
+    da = torch.from_numpy(a).to(dev)
+    db = torch.from_numpy(bt).to(dev)
+    c = torch.empty((4096, 4096), device=dev)
+    sp = {}
+    for chains, lolo in ((1, 0), (2, 0), (3, 0), (3, 1)):
+        ms = best_of(lambda: mfl.gemm_split_fp32(mfl.BF16, 4096, 4096, 4096, da, 4096, 0, 1, db, 4096, 1, 1, chains,
+                                                 lolo, c, 4096, 0, stream), stream, rounds=2, per=5)
+        nprod = 3 + lolo
+        sp[f"chains{chains}{'+lolo' if lolo else ''}"] = {
+            "us": round(ms * 1e3, 1), "useful_tflops": round(2 * 4096 ** 3 / ms / 1e9, 1),
+            "mfma_tflops": round(nprod * 2 * 4096 ** 3 / ms / 1e9, 1)}
+    out["split_4096"] = sp
+    del da, db, c
+
+    # attention pair 2048 x 32768 x 128
+    q, k, v = inputs.attention()
+    dq, dk, dv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    wsb = mfl.attention_workspace_bytes(2048, 32768, 128)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    o = torch.empty((2048, 128), device=dev)
+    att = {}
+    for chains in (1, 2):
+        ms = best_of(lambda: mfl.attention_split_fp32(2048, 32768, 128, dq, dk, dv, chains, o, ws, wsb, stream),
+                     stream, rounds=2, per=5)
+        att[f"chains{chains}_ms"] = round(ms, 3)
+    out["attention_2048x32768"] = att
+    return out
+
+
+def main():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--shape", type=int, default=0, help="MFMA shape of the GEMM fast path (0: 16x16x32, 1: 32x32x16)")
+    p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = p.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM shards by output "
+              "blocks with no exchange, so N GPUs would run N independent copies.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mma_fragment_layouts_amd as mfl
+    from mma_fragment_layouts_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mfl.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    M = N = K = 4096
+    LD = 4096 + 64
+    log("generating inputs")
+    a, bt = inputs.gemm_dense()
+    da32 = torch.from_numpy(a).to(dev)
+    db32 = torch.from_numpy(bt).to(dev)
+    da = torch.empty(da32.shape, dtype=torch.int16, device=dev)
+    db = torch.empty(db32.shape, dtype=torch.int16, device=dev)
+    mfl.quantize_fp32(mfl.BF16, da32, da, da32.numel(), stream)
+    mfl.quantize_fp32(mfl.BF16, db32, db, db32.numel(), stream)
+    del da32, db32
+    c = torch.empty((M, N), device=dev)
+
+    def step():
+        mfl.gemm_tile_mma_shape(args.shape, mfl.BF16, M, N, K, da, LD, mfl.ROW_MAJOR, db, LD, mfl.COL_MAJOR, c, N, 0,
+                                stream)
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("timing", args.steps, "steps")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    flops = 2.0 * M * N * K
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    log(f"{value:.1f} TFLOP/s wall, {achieved:.1f} TFLOP/s by events, {kernel_ms * 1e3:.1f} us/launch")
+
+    result = {
+        "metric": "GEMM TFLOP/s (bf16/fp16->fp32, 4096^3) and % of MI355X MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dense GEMM M=N=K=4096, bf16 A row-major / B col-major, lda=ldb=4160 (NaN pad), "
+                               "fp32 accumulate, fp32 C ldc=4096",
+                   "m": M, "n": N, "k": K, "lda": LD, "ldb": LD, "ldc": N,
+                   "mfma": "16x16x32" if args.shape == 0 else "32x32x16", "tile": "256x256x64, 4 waves"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel_us": round(kernel_ms * 1e3, 2)},
+    }
+    if not args.no_extra:
+        log("other workloads")
+        result["workloads"] = extra_workloads(torch, mfl, inputs, stream)
+    if not args.no_cpu:
+        log("cpu oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(a, bt)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

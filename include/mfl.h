@@ -1,0 +1,204 @@
+/*
+ * mfl.h — C ABI of libmfl.so: MFMA fragment layouts and tiled mixed-precision
+ * GEMMs for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Return value: an mfl_status (0 on success, negative on error).  Nothing is
+ *    thrown across the ABI and there is no global error state; errors are found
+ *    before any HIP call is made, so a rejected call has no side effect.
+ *  - Matrix pointers are DEVICE pointers owned by the caller.  The library never
+ *    allocates or frees device memory; scratch space, where an operation needs
+ *    it, is a caller-provided workspace whose size a query function returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Device calls only enqueue work and return; results are ready when the
+ *    stream is synchronised.  Calls on one stream are ordered; calls on
+ *    different streams that write the same memory race.
+ *  - Matrices: A is M x K, B is K x N, C is M x N.  A row-major A stores
+ *    A[m][k] at a[m*lda + k]; a column-major A stores it at a[k*lda + m].  A
+ *    row-major B stores B[k][n] at b[k*ldb + n]; a column-major B at
+ *    b[n*ldb + k].  C is always row-major: C[m][n] at c[m*ldc + n].  The leading
+ *    dimension is the element distance between successive rows (row-major) or
+ *    columns (column-major) and may exceed the visible extent (padding); each
+ *    operand's storage must span (outer extent) x ld elements.  (Tensor-core
+ *    layout explainer, paragraph on leading dimensions.)
+ *  - 16-bit operands need 16-byte aligned base pointers and ld a multiple of 8;
+ *    fp32 operands 16-byte aligned base pointers and ld a multiple of 4.
+ *    C needs 4-byte alignment only.  Violations return MFL_EINVAL.
+ *  - Any M, N, K >= 0 is accepted (ragged edges are masked); M or N = 0 is a
+ *    no-op; K = 0 gives C = 0 (or leaves C unchanged when accumulating).
+ */
+#ifndef MFL_H
+#define MFL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MFL_API __attribute__((visibility("default")))
+#else
+#define MFL_API
+#endif
+
+typedef enum {
+  MFL_OK = 0,
+  MFL_EINVAL = -1,        /* bad argument: null pointer, out-of-range index, bad ld/alignment */
+  MFL_EOVERFLOW = -2,     /* the result would not fit (the cuda-oxide page's "None on overflow") */
+  MFL_EUNSUPPORTED = -3,  /* valid request this build does not implement */
+  MFL_EHIP = -4           /* a HIP launch failed (hipGetLastError after enqueue) */
+} mfl_status;
+
+typedef enum { MFL_MFMA_16X16X32 = 0, MFL_MFMA_32X32X16 = 1 } mfl_shape;
+typedef enum { MFL_F16 = 0, MFL_BF16 = 1 } mfl_dtype;
+typedef enum { MFL_ROW_MAJOR = 0, MFL_COL_MAJOR = 1 } mfl_order;
+typedef enum { MFL_ROUND = 0, MFL_SPLIT = 1 } mfl_opmode;
+
+/* Human-readable name of a status code (static string, never NULL). */
+MFL_API const char *mfl_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+MFL_API int mfl_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Accumulator-fragment layout (host only, pure functions, no HIP calls).
+ *
+ * cuda-oxide PR #474, section "API": position, row-major offset, strided
+ * destination and inverse of an MMA accumulator fragment element, derived once
+ * as a mixed-radix numeral (section "The layout is a mixed-radix numeral") so
+ * call sites do not re-derive it.  Here the maps are those of the CDNA4
+ * instructions, identical for f16 and bf16 operands:
+ *   MFL_MFMA_16X16X32 (v_mfma_f32_16x16x32_{f16,bf16}): 64 lanes x J=4, 16x16
+ *   MFL_MFMA_32X32X16 (v_mfma_f32_32x32x16_{f16,bf16}): 64 lanes x J=16, 32x32
+ * A (lane, j) pair with lane outside [0,64) or j outside [0,J), an unknown
+ * shape or a NULL output pointer returns MFL_EINVAL and writes nothing.
+ * ------------------------------------------------------------------------- */
+
+/* Tile geometry of `shape`: lanes (64), values per lane J, rows and cols. */
+MFL_API int mfl_acc_info(int shape, int *lanes, int *per_lane, int *rows, int *cols);
+
+/* Position (row, col) of accumulator value j of `lane` within the tile. */
+MFL_API int acc_coords(int shape, int lane, int j, int *row, int *col);
+
+/* Row-major offset row*cols + col of (lane, j), computed in numeral form. */
+MFL_API int acc_offset(int shape, int lane, int j, int *offset);
+
+/* Inverse of acc_offset: the (lane, j) that owns `offset` in [0, rows*cols).
+ * Exported so a caller can round-trip a hand-written layout in a test. */
+MFL_API int acc_decode(int shape, int offset, int *lane, int *j);
+
+/* Strided destination of (lane, j) for a tile whose element origin is
+ * (row0, col0) in a row-major matrix with leading dimension ld:
+ *   *out = (row0 + row) * ld + (col0 + col).
+ * MFL_EOVERFLOW (the page's None) when the value does not fit int64 or when
+ * col0 + col >= ld (the element would spill into the next row, breaking
+ * disjointness of strided placement).  Negative row0/col0 or ld <= 0:
+ * MFL_EINVAL. */
+MFL_API int acc_matrix_offset(int shape, int lane, int j, int64_t row0, int64_t col0, int64_t ld,
+                      int64_t *out);
+
+/* ---------------------------------------------------------------------------
+ * Device entry points.
+ * ------------------------------------------------------------------------- */
+
+/* Strided epilogue store (device): one wave scatters a lane-major accumulator
+ * acc[lane*J + j] (64*J fp32, device memory) into C at element origin
+ * (row0, col0) of a row-major fp32 matrix with leading dimension ldc, writing
+ * C[(row0+row)*ldc + col0+col] = acc[lane*J + j] through the layout above —
+ * one store per accumulator value (Warp issue #1965, "Proposed change": the
+ * accumulator is materialised once).  MFL_EOVERFLOW if col0 + cols > ldc. */
+MFL_API int acc_store_strided(int shape, const float *acc, float *c, int64_t row0, int64_t col0,
+                      int64_t ldc, void *stream);
+
+/* Single-instruction probe (device): one wave executes one MFMA of `shape` and
+ * `dtype` (MFL_F16 or MFL_BF16) with zero accumulator input.  a_frag and b_frag
+ * hold each lane's 8 16-bit operand values lane-major (lane*8 + i); the raw
+ * accumulator registers are written lane-major to acc (lane*J + j).  No layout
+ * logic runs on the device: the caller gathers the operands and scatters the
+ * result, which is how the layout is checked against hardware (cuda-oxide PR
+ * #474, "Verified against hardware"). */
+MFL_API int mfma_probe(int shape, int dtype, const void *a_frag, const void *b_frag, float *acc,
+               void *stream);
+
+/* Round n fp32 values to `dtype` (round-to-nearest-even; NaN stays NaN,
+ * overflow gives +-inf).  out receives n 16-bit values.  Tensor-core layout
+ * explainer, paragraph on mixed precision: conversion changes the values that
+ * enter the multiply. */
+MFL_API int quantize_fp32(int dtype, const float *x, void *out, int64_t n, void *stream);
+
+/* Split n fp32 values into hi = RNE(x) and lo = RNE(x - hi), both `dtype`
+ * (Strata PR #800, "What's going on"). */
+MFL_API int split_fp32(int dtype, const float *x, void *hi, void *lo, int64_t n, void *stream);
+
+/* Tiled mixed-precision GEMM: C = A*B (accumulate = 0) or C += A*B
+ * (accumulate = 1) with `dtype` operands (MFL_F16 or MFL_BF16) and fp32
+ * accumulation kept in registers across the whole K loop; each output tile is
+ * stored once through the accumulator layout (Warp issue #1965, "Proposed
+ * change" and "Design consequences").  Operand orders are free; the fast path
+ * is row-major A with column-major B (both K-contiguous). */
+MFL_API int gemm_tile_mma(int dtype, int64_t m, int64_t n, int64_t k,
+                  const void *a, int64_t lda, int order_a,
+                  const void *b, int64_t ldb, int order_b,
+                  float *c, int64_t ldc, int accumulate, void *stream);
+
+/* Block-GEMM repeat (Warp issue #1965, "Spike"): the output C (m x n, fp32,
+ * row-major, ldc = n) is cut into tm x tn tiles; the workgroup of tile (bi, bj)
+ * loads A[bi*tm.., 0..tk) (a: row-major m x tk, lda = tk) and
+ * B[0..tk, bj*tn..) (b: column-major tk x n, ldb = tk) into LDS once and runs
+ * `repeats` back-to-back tm x tn x tk block MMAs into one register accumulator,
+ * reading the operand fragments from LDS on every repeat, then stores the tile
+ * once: C = repeats * A*B.  Supported (tm, tn, tk, threads): (64,64,64, 64|128|256),
+ * (32,32,32, 128), (128,128,32, 128|256); m % tm == 0 and n % tn == 0;
+ * others return MFL_EUNSUPPORTED. */
+MFL_API int gemm_block_repeat(int dtype, int tm, int tn, int tk, int threads, int repeats,
+                      int64_t m, int64_t n, const void *a, const void *b, float *c,
+                      void *stream);
+
+/* Split-precision fp32 GEMM (Strata PR #800, "The fix"): A and B are fp32; an
+ * operand in MFL_SPLIT mode is split on load into hi = RNE(x) and
+ * lo = RNE(x - hi) of type `piece` (MFL_F16 or MFL_BF16), an operand in
+ * MFL_ROUND mode is rounded once.  Products per K step: hi*hi, hi*lo, lo*hi
+ * (those that exist for the modes), plus lo*lo if `lolo` and both are split.
+ *   chains = 1: every product goes into one accumulator (the single-chain
+ *               variant, kept for comparison);
+ *   chains = 2: hi*hi in one accumulator, all correction products in a second;
+ *   chains = 3: hi*hi, hi*lo and lo*hi(+lo*lo) in three (both operands split).
+ * The chains are summed in plain fp32 once, at the end: hh + (hl + lh).
+ * C = result (accumulate = 0) or C += result (accumulate = 1). */
+MFL_API int gemm_split_fp32(int piece, int64_t m, int64_t n, int64_t k,
+                    const float *a, int64_t lda, int order_a, int mode_a,
+                    const float *b, int64_t ldb, int order_b, int mode_b,
+                    int chains, int lolo, float *c, int64_t ldc, int accumulate,
+                    void *stream);
+
+/* gemm_tile_mma with an explicit MFMA instruction for the fast path
+ * (MFL_MFMA_16X16X32 or MFL_MFMA_32X32X16); gemm_tile_mma uses 16x16x32.  The
+ * generic path (other orders, ragged sizes) always uses 16x16x32. */
+MFL_API int gemm_tile_mma_shape(int shape, int dtype, int64_t m, int64_t n, int64_t k,
+                                const void *a, int64_t lda, int order_a,
+                                const void *b, int64_t ldb, int order_b,
+                                float *c, int64_t ldc, int accumulate, void *stream);
+
+/* Bytes of device workspace attention_split_fp32 needs for these sizes. */
+MFL_API int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int64_t *bytes);
+
+/* Attention-shaped pair of split GEMMs, one head (Strata PR #800): q (nq x d),
+ * k and v (nk x d), o (nq x d), all fp32 row-major with ld = d.
+ *   S = Q K^T with Q split into f16 hi/lo and K rounded once to f16;
+ *   m = rowmax S, P~ = exp(S - m), l = rowsum P~ (fp32);
+ *   O = (P~ V) / l with P~ split into f16 hi/lo and V rounded once to f16.
+ * `chains` (1 or 2) selects single-chain or separate hi/lo accumulators for
+ * both products.  No causal mask and no 1/sqrt(d) scaling are applied.
+ * Supported: d = 128, nq and nk multiples of 128.  `workspace` is device memory
+ * of at least attention_workspace_bytes() bytes, 256-byte aligned. */
+MFL_API int attention_split_fp32(int64_t nq, int64_t nk, int64_t d, const float *q, const float *k,
+                         const float *v, int chains, float *o, void *workspace,
+                         int64_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MFL_H */

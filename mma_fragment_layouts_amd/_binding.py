@@ -1,0 +1,198 @@
+"""ctypes binding of libmfl.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls (include/mfl.h)
+and does nothing but convert arguments (device pointers from ints or from
+objects with ``data_ptr()``, streams from ints or from objects with
+``cuda_stream``), call the library and turn a non-zero status into
+``MflError``.  All computation happens in the library's HIP kernels; if the
+library is missing, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Tuple
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmfl.so")
+
+# enums (values fixed by include/mfl.h)
+OK, EINVAL, EOVERFLOW, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
+MFMA_16X16X32, MFMA_32X32X16 = 0, 1
+F16, BF16 = 0, 1
+ROW_MAJOR, COL_MAJOR = 0, 1
+ROUND, SPLIT = 0, 1
+
+_i32, _i64, _vp = C.c_int, C.c_int64, C.c_void_p
+_pi32, _pi64 = C.POINTER(C.c_int), C.POINTER(C.c_int64)
+
+_SIGNATURES = {
+    "mfl_status_string": (C.c_char_p, [_i32]),
+    "mfl_version": (_i32, []),
+    "mfl_acc_info": (_i32, [_i32, _pi32, _pi32, _pi32, _pi32]),
+    "acc_coords": (_i32, [_i32, _i32, _i32, _pi32, _pi32]),
+    "acc_offset": (_i32, [_i32, _i32, _i32, _pi32]),
+    "acc_decode": (_i32, [_i32, _i32, _pi32, _pi32]),
+    "acc_matrix_offset": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _pi64]),
+    "acc_store_strided": (_i32, [_i32, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "mfma_probe": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp]),
+    "quantize_fp32": (_i32, [_i32, _vp, _vp, _i64, _vp]),
+    "split_fp32": (_i32, [_i32, _vp, _vp, _vp, _i64, _vp]),
+    "gemm_tile_mma": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _vp, _i64, _i32, _vp]),
+    "gemm_tile_mma_shape": (_i32, [_i32, _i32, _i64, _i64, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _vp, _i64,
+                                   _i32, _vp]),
+    "gemm_block_repeat": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "gemm_split_fp32": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _i64, _i32, _i32, _i32, _i32,
+                               _vp, _i64, _i32, _vp]),
+    "attention_workspace_bytes": (_i32, [_i64, _i64, _i64, _pi64]),
+    "attention_split_fp32": (_i32, [_i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _vp]),
+}
+EXPORTS = tuple(_SIGNATURES)
+
+_lib: Optional[C.CDLL] = None
+
+
+class MflError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load() -> C.CDLL:
+    """Load libmfl.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libmfl.so not found at {LIB_PATH}; build it with "
+                               "`python -m mma_fragment_layouts_amd.build`")
+        lib = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    raise TypeError(f"expected a device pointer (int or tensor), got {type(x)}")
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    raise TypeError(f"expected a stream handle, got {type(s)}")
+
+
+def _check(st: int, fn: str) -> None:
+    if st != OK:
+        raise MflError(st, fn)
+
+
+def status_string(status: int) -> str:
+    return load().mfl_status_string(status).decode()
+
+
+def mfl_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def mfl_version() -> int:
+    return load().mfl_version()
+
+
+def mfl_acc_info(shape: int) -> Tuple[int, int, int, int]:
+    v = [C.c_int() for _ in range(4)]
+    _check(load().mfl_acc_info(shape, *[C.byref(x) for x in v]), "mfl_acc_info")
+    return tuple(x.value for x in v)
+
+
+def acc_coords(shape: int, lane: int, j: int) -> Tuple[int, int]:
+    r, c = C.c_int(), C.c_int()
+    _check(load().acc_coords(shape, lane, j, C.byref(r), C.byref(c)), "acc_coords")
+    return r.value, c.value
+
+
+def acc_offset(shape: int, lane: int, j: int) -> int:
+    o = C.c_int()
+    _check(load().acc_offset(shape, lane, j, C.byref(o)), "acc_offset")
+    return o.value
+
+
+def acc_decode(shape: int, offset: int) -> Tuple[int, int]:
+    lane, j = C.c_int(), C.c_int()
+    _check(load().acc_decode(shape, offset, C.byref(lane), C.byref(j)), "acc_decode")
+    return lane.value, j.value
+
+
+def acc_matrix_offset(shape: int, lane: int, j: int, row0: int, col0: int, ld: int) -> Optional[int]:
+    """Strided destination, or None when the library reports MFL_EOVERFLOW."""
+    o = C.c_int64()
+    st = load().acc_matrix_offset(shape, lane, j, row0, col0, ld, C.byref(o))
+    if st == EOVERFLOW:
+        return None
+    _check(st, "acc_matrix_offset")
+    return o.value
+
+
+def acc_store_strided(shape, acc, c, row0, col0, ldc, stream=None) -> None:
+    _check(load().acc_store_strided(shape, _ptr(acc), _ptr(c), row0, col0, ldc, _stream(stream)),
+           "acc_store_strided")
+
+
+def mfma_probe(shape, dtype, a_frag, b_frag, acc, stream=None) -> None:
+    _check(load().mfma_probe(shape, dtype, _ptr(a_frag), _ptr(b_frag), _ptr(acc), _stream(stream)), "mfma_probe")
+
+
+def quantize_fp32(dtype, x, out, n, stream=None) -> None:
+    _check(load().quantize_fp32(dtype, _ptr(x), _ptr(out), n, _stream(stream)), "quantize_fp32")
+
+
+def split_fp32(dtype, x, hi, lo, n, stream=None) -> None:
+    _check(load().split_fp32(dtype, _ptr(x), _ptr(hi), _ptr(lo), n, _stream(stream)), "split_fp32")
+
+
+def gemm_tile_mma(dtype, m, n, k, a, lda, order_a, b, ldb, order_b, c, ldc, accumulate=0, stream=None) -> None:
+    _check(load().gemm_tile_mma(dtype, m, n, k, _ptr(a), lda, order_a, _ptr(b), ldb, order_b, _ptr(c), ldc,
+                                accumulate, _stream(stream)), "gemm_tile_mma")
+
+
+def gemm_tile_mma_shape(shape, dtype, m, n, k, a, lda, order_a, b, ldb, order_b, c, ldc, accumulate=0,
+                        stream=None) -> None:
+    _check(load().gemm_tile_mma_shape(shape, dtype, m, n, k, _ptr(a), lda, order_a, _ptr(b), ldb, order_b, _ptr(c),
+                                      ldc, accumulate, _stream(stream)), "gemm_tile_mma_shape")
+
+
+def gemm_block_repeat(dtype, tm, tn, tk, threads, repeats, m, n, a, b, c, stream=None) -> None:
+    _check(load().gemm_block_repeat(dtype, tm, tn, tk, threads, repeats, m, n, _ptr(a), _ptr(b), _ptr(c),
+                                    _stream(stream)), "gemm_block_repeat")
+
+
+def gemm_split_fp32(piece, m, n, k, a, lda, order_a, mode_a, b, ldb, order_b, mode_b, chains, lolo, c, ldc,
+                    accumulate=0, stream=None) -> None:
+    _check(load().gemm_split_fp32(piece, m, n, k, _ptr(a), lda, order_a, mode_a, _ptr(b), ldb, order_b, mode_b,
+                                  chains, lolo, _ptr(c), ldc, accumulate, _stream(stream)), "gemm_split_fp32")
+
+
+def attention_workspace_bytes(nq, nk, d) -> int:
+    b = C.c_int64()
+    _check(load().attention_workspace_bytes(nq, nk, d, C.byref(b)), "attention_workspace_bytes")
+    return b.value
+
+
+def attention_split_fp32(nq, nk, d, q, k, v, chains, o, workspace, workspace_bytes, stream=None) -> None:
+    _check(load().attention_split_fp32(nq, nk, d, _ptr(q), _ptr(k), _ptr(v), chains, _ptr(o), _ptr(workspace),
+                                       workspace_bytes, _stream(stream)), "attention_split_fp32")

@@ -1,0 +1,198 @@
+// The tiled MFMA GEMM core: global -> swizzled LDS tile loaders, the LDS ->
+// fragment -> MFMA step with register-resident accumulators, and the epilogue
+// that stores each accumulator value once through the fragment layout.
+//
+// Warp issue #1965 ("Description", "Proposed change") names the two costs a
+// shared-memory-operand GEMM pays — fragment loads from plain shared layouts hit
+// bank conflicts, and C is read and written through shared memory on every call
+// — and the cure: swizzled operand tiles plus an accumulator that lives in
+// registers across the K loop and is materialised once.  These templates are
+// that design for CDNA4 wavefronts of 64 lanes.
+#pragma once
+#include "common.hpp"
+
+namespace mfl {
+
+// Loads one R x BK operand tile (16-bit elements) from global memory into
+// registers and later writes it to the swizzled LDS tile.
+//   KC = true : element (r, k) of the tile is at base[(r0 + r)*ld + k0 + k]
+//               (row-major A or column-major B: K contiguous); 16-byte loads
+//               along K, 16-byte LDS writes.
+//   KC = false: element (r, k) is at base[(k0 + k)*ld + r0 + r] (K strided);
+//               16-byte loads along R, scattered 2-byte LDS writes.
+// EDGE enables masking: K positions >= k_total are zero (in both operands, so a
+// NaN in padding never meets a zero), R positions past rows_total are read from
+// in-bounds storage but never stored by the epilogue.
+template <int R, int BK, int NT, bool KC, bool EDGE>
+struct TileLoader {
+  static constexpr int CHUNKS = R * BK / 8;
+  static constexpr int PER = CHUNKS / NT;
+  static_assert(CHUNKS % NT == 0, "tile chunks must divide evenly among threads");
+  u32x4 reg[PER];
+
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld, int r0, int k0, int rows_total,
+                                       int k_total, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      if constexpr (KC) {
+        const int r = idx / (BK / 8), c = idx % (BK / 8);
+        int gr = r0 + r;
+        const int kf = k0 + c * 8;
+        if constexpr (EDGE) {
+          gr = min(gr, rows_total - 1);
+          if (kf + 8 <= k_total)
+            reg[i] = gload16(base + (int64_t)gr * ld + kf);
+          else if (kf < k_total)
+            reg[i] = mask_tail(gload16(base + (int64_t)gr * ld + kf), kf, k_total);
+          else
+            reg[i] = u32x4{0, 0, 0, 0};
+        } else {
+          reg[i] = gload16(base + (int64_t)gr * ld + kf);
+        }
+      } else {
+        const int k = idx / (R / 8), rc = idx % (R / 8);
+        const int gk = k0 + k, gr = r0 + rc * 8;
+        if (!EDGE || (gk < k_total && gr < rows_total))
+          reg[i] = gload16(base + (int64_t)gk * ld + gr);
+        else
+          reg[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      if constexpr (KC) {
+        const int r = idx / (BK / 8), c = idx % (BK / 8);
+        lds_write16(lds, lds_chunk<BK>(r, c), reg[i]);
+      } else {
+        const int k = idx / (R / 8), rc = idx % (R / 8);
+        uint16_t h[8];
+        __builtin_memcpy(h, &reg[i], 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lds[lds_elem<BK>(rc * 8 + e, k)] = h[e];
+      }
+    }
+  }
+};
+
+// Reads MFMA operand fragments from the swizzled LDS tiles.  Lane l takes row
+// (l mod MN) of each MN-row fragment and the 16-byte chunk (l div MN) of the
+// current MFMA K step.  The per-lane offsets of the BK/KM K steps are computed
+// once; fragment i of the wave adds the immediate i*MN*BK.
+template <int SHAPE, int BK>
+struct FragOffsets {
+  static constexpr int MN = Shape<SHAPE>::MN, KM = Shape<SHAPE>::K, CPK = KM / 8, KSTEPS = BK / KM;
+  int off[KSTEPS];
+  __device__ __forceinline__ FragOffsets(int row0, int lane) {
+    const int lr = lane % MN, lk = lane / MN;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) off[kk] = lds_chunk<BK>(row0 + lr, kk * CPK + lk);
+  }
+};
+
+// One BK-deep slab of the wave's TM x TN grid of MFMA tiles: for each MFMA K
+// step, read the A and B fragments from LDS and accumulate into registers.
+template <int SHAPE, int DT, int TM, int TN, int BK>
+__device__ __forceinline__ void mma_slab(const uint16_t* sA, const uint16_t* sB, const FragOffsets<SHAPE, BK>& fa,
+                                         const FragOffsets<SHAPE, BK>& fb,
+                                         typename Shape<SHAPE>::Acc (&acc)[TM][TN]) {
+  constexpr int MN = Shape<SHAPE>::MN;
+#pragma unroll
+  for (int kk = 0; kk < FragOffsets<SHAPE, BK>::KSTEPS; ++kk) {
+    u32x4 a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = lds_read16(sA, fa.off[kk] + i * MN * BK);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = lds_read16(sB, fb.off[kk] + j * MN * BK);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma<SHAPE, DT>(a[i], b[j], acc[i][j]);
+  }
+}
+
+// Epilogue: every accumulator value goes to C[(row0+row)*ldc + col0+col] with
+// (row, col) from the instruction's accumulator layout — one store per value.
+// ACCUM adds to the existing C instead of overwriting it.
+template <int SHAPE, int TM, int TN, bool EDGE, bool ACCUM>
+__device__ __forceinline__ void store_acc_impl(float* __restrict__ C, int64_t ldc, int row0, int col0, int M, int N,
+                                               int lane, const typename Shape<SHAPE>::Acc (&acc)[TM][TN]) {
+  constexpr AccLayout L = acc_layout(SHAPE);
+  constexpr int MN = Shape<SHAPE>::MN, J = Shape<SHAPE>::J;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < J; ++v) {
+        const int r = row0 + i * MN + acc_row(L, lane, v);
+        const int c = col0 + j * MN + acc_col(L, lane, v);
+        if (!EDGE || (r < M && c < N)) {
+          float* p = C + (int64_t)r * ldc + c;
+          if constexpr (ACCUM)
+            *p += acc[i][j][v];
+          else
+            *p = acc[i][j][v];
+        }
+      }
+}
+
+template <int SHAPE, int TM, int TN, bool EDGE>
+__device__ __forceinline__ void store_acc(float* __restrict__ C, int64_t ldc, int row0, int col0, int M, int N,
+                                          int lane, const typename Shape<SHAPE>::Acc (&acc)[TM][TN], int accumulate) {
+  if (accumulate)
+    store_acc_impl<SHAPE, TM, TN, EDGE, true>(C, ldc, row0, col0, M, N, lane, acc);
+  else
+    store_acc_impl<SHAPE, TM, TN, EDGE, false>(C, ldc, row0, col0, M, N, lane, acc);
+}
+
+// The accumulator numeral's j digits all sit at multiples of the tile width, so
+// (row, col)(lane, j) = (row, col)(lane, 0) + (row(0, j), 0): a per-lane part and
+// a part that is uniform across the wave.  The buffer-store epilogue relies on it.
+constexpr bool acc_rows_separable(const AccLayout& L) {
+  for (int lane = 0; lane < L.lanes; ++lane)
+    for (int j = 0; j < L.per_lane; ++j)
+      if (acc_col(L, lane, j) != acc_col(L, lane, 0) || acc_col(L, 0, j) != 0 ||
+          acc_row(L, lane, j) != acc_row(L, lane, 0) + acc_row(L, 0, j))
+        return false;
+  return true;
+}
+static_assert(acc_rows_separable(kAcc16x16x32) && acc_rows_separable(kAcc32x32x16), "layout j digits must be rows");
+
+// Epilogue through a buffer resource whose base is the wave tile's origin in C:
+// one 32-bit per-lane offset, uniform row offsets from the j digits.
+template <int SHAPE, int TM, int TN, bool ACCUM>
+__device__ __forceinline__ void store_acc_rsrc(rsrc_t c, uint32_t ldc, int lane,
+                                               const typename Shape<SHAPE>::Acc (&acc)[TM][TN]) {
+  constexpr AccLayout L = acc_layout(SHAPE);
+  constexpr int MN = Shape<SHAPE>::MN, J = Shape<SHAPE>::J;
+  const uint32_t voff = ((uint32_t)acc_row(L, lane, 0) * ldc + (uint32_t)acc_col(L, lane, 0)) * 4u;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int v = 0; v < J; ++v) {
+      const uint32_t srow = (uint32_t)(i * MN + acc_row(L, 0, v)) * ldc * 4u;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        float x = acc[i][j][v];
+        if constexpr (ACCUM) x += __builtin_amdgcn_raw_buffer_load_b32(c, voff + j * MN * 4, srow, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(x, c, voff + j * MN * 4, srow, 0);
+      }
+    }
+}
+
+template <int SHAPE, int TM, int TN>
+__device__ __forceinline__ void zero_acc(typename Shape<SHAPE>::Acc (&acc)[TM][TN]) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < Shape<SHAPE>::J; ++v) acc[i][j][v] = 0.f;
+}
+
+}  // namespace mfl

@@ -1,0 +1,243 @@
+// gemm_tile_mma: tiled fp16/bf16 -> fp32 GEMM on CDNA4 MFMA.
+//
+// Each workgroup owns one BM x BN output tile.  The K loop streams 64-deep
+// slabs of A and B through a double-buffered, swizzled LDS tile (the next slab
+// is in flight while the current one feeds the MFMAs), the fp32 accumulators
+// stay in registers for the whole loop, and the tile is stored once at the end
+// (Warp issue #1965, "Proposed change" and "Design consequences").
+#include "gemm_core.hpp"
+
+namespace mfl {
+
+// ---------------------------------------------------------------------------
+// Generic path: any operand orders, any M, N, K (ragged edges masked).  The
+// next slab is staged in registers, then written to the LDS buffer not being
+// read.
+template <int BM, int BN, int BK, int WGM, int WGN, int SHAPE, int DT, bool AK, bool BKC, bool EDGE>
+__global__ __launch_bounds__(WGM* WGN * 64) void gemm_tile_kernel(const uint16_t* __restrict__ A,
+                                                                   const uint16_t* __restrict__ B,
+                                                                   float* __restrict__ C, int64_t lda, int64_t ldb,
+                                                                   int64_t ldc, int M, int N, int K, int tiles_m,
+                                                                   int tiles_n, int accumulate) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int MN = Shape<SHAPE>::MN;
+  constexpr int TM = WM / MN, TN = WN / MN;
+  static_assert(TM * MN == WM && TN * MN == WN, "wave tile must be a multiple of the MFMA tile");
+  constexpr int STAGE = (BM + BN) * BK;
+  using Acc = typename Shape<SHAPE>::Acc;
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, &tm, &tn);
+  const int row0 = tm * BM, col0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr0 = (wave / WGN) * WM, wc0 = (wave % WGN) * WN;
+  const FragOffsets<SHAPE, BK> fa(wr0, lane), fb(wc0, lane);
+
+  Acc acc[TM][TN];
+  zero_acc<SHAPE, TM, TN>(acc);
+
+  TileLoader<BM, BK, NT, AK, EDGE> la;
+  TileLoader<BN, BK, NT, BKC, EDGE> lb;
+  const int KT = (K + BK - 1) / BK;
+  if (KT > 0) {
+    la.load(A, lda, row0, 0, M, K, tid);
+    lb.load(B, ldb, col0, 0, N, K, tid);
+    la.store(lds, tid);
+    lb.store(lds + BM * BK, tid);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = (kt & 1) * STAGE, nxt = STAGE - cur;
+      const bool more = kt + 1 < KT;
+      if (more) {
+        la.load(A, lda, row0, (kt + 1) * BK, M, K, tid);
+        lb.load(B, ldb, col0, (kt + 1) * BK, N, K, tid);
+      }
+      mma_slab<SHAPE, DT, TM, TN, BK>(lds + cur, lds + cur + BM * BK, fa, fb, acc);
+      if (more) {
+        la.store(lds + nxt, tid);
+        lb.store(lds + nxt + BM * BK, tid);
+      }
+      __syncthreads();
+    }
+  }
+  store_acc<SHAPE, TM, TN, EDGE>(C, ldc, row0 + wr0, col0 + wc0, M, N, lane, acc, accumulate);
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int SHAPE, int DT, bool AK, bool BKC, bool EDGE>
+static int launch_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, float* c, int64_t ldc, int M, int N,
+                       int K, int accumulate, hipStream_t stream) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, BK, WGM, WGN, SHAPE, DT, AK, BKC, EDGE>), dim3(tiles_m * tiles_n),
+                     dim3(WGM * WGN * 64), 0, stream, (const uint16_t*)a, (const uint16_t*)b, c, lda, ldb, ldc, M, N,
+                     K, tiles_m, tiles_n, accumulate);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Fast path: both operands K-contiguous, M % BM == 0, N % BN == 0, K % 64 == 0.
+// Global -> LDS moves use the CDNA4 direct-to-LDS buffer load
+// (buffer_load_dwordx4 ... lds): one wave instruction writes 64 x 16 bytes to
+// consecutive LDS addresses, so a wave fills 8 rows of a 128-byte-per-row tile
+// with no staging registers.  The swizzle is applied on the source side: the
+// lane that lands in physical chunk p of row r fetches logical chunk p ^ swz(r).
+// Per-lane state is one 32-bit offset per operand; the row step of each load
+// instruction and the K step are uniform scalar offsets.
+template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT>
+__global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t* __restrict__ A,
+                                                                   const uint16_t* __restrict__ B,
+                                                                   float* __restrict__ C, uint32_t lda, uint32_t ldb,
+                                                                   uint32_t ldc, int K, int tiles_m, int tiles_n,
+                                                                   int accumulate) {
+  constexpr int BK = 64;
+  constexpr int NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int MN = Shape<SHAPE>::MN;
+  constexpr int TM = WM / MN, TN = WN / MN;
+  constexpr int STAGE = (BM + BN) * BK;
+  constexpr int A_INSTR = BM / 8 / NW, B_INSTR = BN / 8 / NW;
+  static_assert(A_INSTR * 8 * NW == BM && B_INSTR * 8 * NW == BN, "tile rows must split into 8-row wave loads");
+  static_assert((NW % 2) == 0, "per-lane swizzle is load-invariant only for an even number of waves");
+  using Acc = typename Shape<SHAPE>::Acc;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
+
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, &tm, &tn);
+  const int row0 = tm * BM, col0 = tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr0 = (wave / WGN) * WM, wc0 = (wave % WGN) * WN;
+
+  // Buffers start at the workgroup's first row of A and of B (column of B).
+  const rsrc_t ra = make_rsrc(A + (int64_t)row0 * lda, (uint32_t)BM * lda * 2u);
+  const rsrc_t rb = make_rsrc(B + (int64_t)col0 * ldb, (uint32_t)BN * ldb * 2u);
+  // Load instruction i of this wave fills tile rows (i*NW + wave)*8 .. +8; lane l
+  // writes row +l/8, physical chunk l%8.  With NW even, (row mod 16) — and so
+  // the swizzle — is the same for every i, so one per-lane offset serves all.
+  const int lrow = wave * 8 + (lane >> 3);
+  const uint32_t va = (uint32_t)lrow * lda * 2u + (uint32_t)(((lane & 7) ^ swz<BK>(lrow)) << 4);
+  const uint32_t vb = (uint32_t)lrow * ldb * 2u + (uint32_t)(((lane & 7) ^ swz<BK>(lrow)) << 4);
+
+  auto issue = [&](int stage, int k0) {
+    uint16_t* base = lds + stage * STAGE + wave * 8 * BK;
+#pragma unroll
+    for (int i = 0; i < A_INSTR; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + i * NW * 8 * BK), 16, va,
+                                               (uint32_t)(i * NW * 8) * lda * 2u + (uint32_t)k0 * 2u, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(base + BM * BK + i * NW * 8 * BK), 16, vb,
+                                               (uint32_t)(i * NW * 8) * ldb * 2u + (uint32_t)k0 * 2u, 0, 0);
+  };
+
+  const FragOffsets<SHAPE, BK> fa(wr0, lane), fb(wc0, lane);
+  Acc acc[TM][TN];
+  zero_acc<SHAPE, TM, TN>(acc);
+
+  const int KT = K / BK;
+  if (KT > 0) {
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < KT) issue(cur ^ 1, (kt + 1) * BK);
+      mma_slab<SHAPE, DT, TM, TN, BK>(lds + cur * STAGE, lds + cur * STAGE + BM * BK, fa, fb, acc);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  }
+  // The store buffer starts at this wave's tile origin and spans its WM rows.
+  const rsrc_t rc = make_rsrc(C + (int64_t)(row0 + wr0) * ldc + col0 + wc0, (uint32_t)WM * ldc * 4u);
+  if (accumulate)
+    store_acc_rsrc<SHAPE, TM, TN, true>(rc, ldc, lane, acc);
+  else
+    store_acc_rsrc<SHAPE, TM, TN, false>(rc, ldc, lane, acc);
+}
+
+template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT>
+static int launch_fast(const void* a, int64_t lda, const void* b, int64_t ldb, float* c, int64_t ldc, int M, int N,
+                       int K, int accumulate, hipStream_t stream) {
+  const int tiles_m = M / BM, tiles_n = N / BN;
+  hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WGM, WGN, SHAPE, DT>), dim3(tiles_m * tiles_n), dim3(WGM * WGN * 64), 0,
+                     stream, (const uint16_t*)a, (const uint16_t*)b, c, (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, K,
+                     tiles_m, tiles_n, accumulate);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+template <int DT, bool AK, bool BKC>
+static int launch_generic(const void* a, int64_t lda, const void* b, int64_t ldb, float* c, int64_t ldc, int M, int N,
+                          int K, int accumulate, hipStream_t s) {
+  if (M % 128 == 0 && N % 128 == 0 && K % 64 == 0)
+    return launch_gemm<128, 128, 64, 2, 2, 0, DT, AK, BKC, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  return launch_gemm<128, 128, 64, 2, 2, 0, DT, AK, BKC, true>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+}
+
+// The buffer offsets of the fast path are 32-bit: the byte extent of a 256-row
+// panel of A, B and of C must stay below 4 GiB.
+static bool fast_fits(int64_t lda, int64_t ldb, int64_t ldc) {
+  const int64_t lim = (int64_t)1 << 32;
+  return 256 * lda * 2 < lim && 256 * ldb * 2 < lim && 256 * ldc * 4 < lim;
+}
+
+template <int DT>
+static int dispatch(int shape, const void* a, int64_t lda, int oa, const void* b, int64_t ldb, int ob, float* c,
+                    int64_t ldc, int M, int N, int K, int accumulate, hipStream_t s) {
+  const bool ak = oa == MFL_ROW_MAJOR, bk = ob == MFL_COL_MAJOR;
+  if (ak && bk && M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && fast_fits(lda, ldb, ldc)) {
+    if (shape == MFL_MFMA_32X32X16)
+      return launch_fast<256, 256, 2, 2, 1, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+    return launch_fast<256, 256, 2, 2, 0, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  }
+  if (ak && bk) return launch_generic<DT, true, true>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  if (ak) return launch_generic<DT, true, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  if (bk) return launch_generic<DT, false, true>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  return launch_generic<DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+}
+
+// Validates one 16-bit operand of `rows` x `cols` (logical) stored in `order`.
+static int check16(const void* p, int64_t rows, int64_t cols, int64_t ld, int order) {
+  if (order != MFL_ROW_MAJOR && order != MFL_COL_MAJOR) return MFL_EINVAL;
+  if (rows == 0 || cols == 0) return MFL_OK;
+  if (!p || !aligned16(p) || ld <= 0 || ld % 8 != 0) return MFL_EINVAL;
+  const int64_t inner = order == MFL_ROW_MAJOR ? cols : rows;
+  const int64_t outer = order == MFL_ROW_MAJOR ? rows : cols;
+  if (ld < inner) return MFL_EINVAL;
+  if (outer > INT64_MAX / ld) return MFL_EOVERFLOW;
+  return MFL_OK;
+}
+
+}  // namespace mfl
+
+using namespace mfl;
+
+extern "C" int gemm_tile_mma_shape(int shape, int dtype, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda,
+                                   int order_a, const void* b, int64_t ldb, int order_b, float* c, int64_t ldc,
+                                   int accumulate, void* stream) {
+  if (shape != MFL_MFMA_16X16X32 && shape != MFL_MFMA_32X32X16) return MFL_EINVAL;
+  if (dtype != MFL_F16 && dtype != MFL_BF16) return MFL_EINVAL;
+  if (m < 0 || n < 0 || k < 0 || (accumulate != 0 && accumulate != 1)) return MFL_EINVAL;
+  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return MFL_EUNSUPPORTED;
+  int st;
+  if ((st = check16(a, m, k, lda, order_a)) != MFL_OK) return st;
+  if ((st = check16(b, k, n, ldb, order_b)) != MFL_OK) return st;
+  if (m == 0 || n == 0) return MFL_OK;
+  if (!c || ((uintptr_t)c & 3) || ldc < n) return MFL_EINVAL;
+  if (m > INT64_MAX / ldc) return MFL_EOVERFLOW;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == MFL_BF16)
+    return dispatch<MFL_BF16>(shape, a, lda, order_a, b, ldb, order_b, c, ldc, (int)m, (int)n, (int)k, accumulate, s);
+  return dispatch<MFL_F16>(shape, a, lda, order_a, b, ldb, order_b, c, ldc, (int)m, (int)n, (int)k, accumulate, s);
+}
+
+extern "C" int gemm_tile_mma(int dtype, int64_t m, int64_t n, int64_t k, const void* a, int64_t lda, int order_a,
+                             const void* b, int64_t ldb, int order_b, float* c, int64_t ldc, int accumulate,
+                             void* stream) {
+  return gemm_tile_mma_shape(MFL_MFMA_16X16X32, dtype, m, n, k, a, lda, order_a, b, ldb, order_b, c, ldc, accumulate,
+                             stream);
+}

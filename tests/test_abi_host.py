@@ -1,0 +1,194 @@
+"""Host-side tests of libmfl.so: it loads, exports every entry point the header
+declares, its layout functions agree bit for bit with the oracle's brute-force
+enumeration, and invalid arguments are rejected before any HIP call (so these
+run without a GPU)."""
+import os
+import re
+
+import pytest
+
+from oracle import layouts as OL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mfl.h")
+SHAPES = {0: OL.MFMA_16X16X32, 1: OL.MFMA_32X32X16}
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^MFL_API\s+(?:const\s+char\s*\*|int)\s*([a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_and_library_exports_every_entry_point(lib):
+    declared = header_functions()
+    assert len(declared) >= 15
+    so = lib.load()
+    for name in declared:
+        assert hasattr(so, name), f"{name} declared in mfl.h but not exported"
+    assert sorted(lib.EXPORTS) == declared
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mfl_version() >= 100
+    assert lib.status_string(0) == "MFL_OK"
+    for st in (-1, -2, -3, -4):
+        assert lib.status_string(st).startswith("MFL_E")
+    assert "unknown" in lib.status_string(17)
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+def test_acc_info(lib, shape):
+    fm = SHAPES[shape]
+    assert lib.mfl_acc_info(shape) == (fm.lanes, fm.per_lane, fm.rows, fm.cols)
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+def test_coords_offsets_decode_match_oracle_exhaustively(lib, shape):
+    """Every (lane, j): the library's numeral-form coordinates and offsets equal
+    the oracle's row/col enumeration; decode equals the oracle's inverted table."""
+    fm = SHAPES[shape]
+    inv = OL.decode_table(fm)
+    for lane in range(fm.lanes):
+        for j in range(fm.per_lane):
+            assert lib.acc_coords(shape, lane, j) == fm.coords(lane, j)
+            assert lib.acc_offset(shape, lane, j) == OL.offset(fm, lane, j)
+    for o in range(fm.rows * fm.cols):
+        assert lib.acc_decode(shape, o) == inv[o]
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+def test_six_layout_properties(lib, shape):
+    """The six checks of the cuda-oxide page's "Tests" section, on the library."""
+    fm = SHAPES[shape]
+    L, J, R, Cc = lib.mfl_acc_info(shape)
+    pts = [(l, j) for l in range(L) for j in range(J)]
+    # 1. bijection via an ownership map (no overlap, no gap)
+    own = [[0] * Cc for _ in range(R)]
+    for l, j in pts:
+        r, c = lib.acc_coords(shape, l, j)
+        own[r][c] += 1
+    assert all(v == 1 for row in own for v in row)
+    # 2. numeral form agrees with the row/col form
+    for l, j in pts:
+        r, c = lib.acc_coords(shape, l, j)
+        assert lib.acc_offset(shape, l, j) == r * Cc + c
+    # 3. decode is a true inverse on all points (both directions)
+    for l, j in pts:
+        assert lib.acc_decode(shape, lib.acc_offset(shape, l, j)) == (l, j)
+    for o in range(R * Cc):
+        assert lib.acc_offset(shape, *lib.acc_decode(shape, o)) == o
+    # 4. the fragment index is split: j 0->1 moves one row; the next digit of j
+    #    (j 0->J/... ) moves further, in rows, never in columns
+    for l in range(L):
+        r0, c0 = lib.acc_coords(shape, l, 0)
+        assert lib.acc_coords(shape, l, 1) == (r0 + 1, c0)
+        if shape == 1:
+            assert lib.acc_coords(shape, l, 4) == (r0 + 8, c0)
+    # 5. disjointness preserved under strided placement
+    ld = 3 * Cc + 8
+    seen = set()
+    for tr in range(3):
+        for tc in range(3):
+            for l, j in pts:
+                o = lib.acc_matrix_offset(shape, l, j, tr * R, tc * Cc, ld)
+                assert o is not None and o not in seen
+                assert o == OL.matrix_offset(fm, l, j, tr * R, tc * Cc, ld)
+                seen.add(o)
+    # 6. overflow rejection
+    assert lib.acc_matrix_offset(shape, L - 1, J - 1, 0, Cc, 2 * Cc - 1) is None   # spills past ld
+    assert lib.acc_matrix_offset(shape, L - 1, J - 1, 1 << 62, 0, 4) is None        # int64 overflow
+    assert OL.matrix_offset(fm, L - 1, J - 1, 1 << 62, 0, 4) is None
+
+
+def test_matrix_offset_matches_oracle_on_random_origins(lib):
+    import random
+    rnd = random.Random(5)
+    for _ in range(2000):
+        shape = rnd.randint(0, 1)
+        fm = SHAPES[shape]
+        lane, j = rnd.randrange(64), rnd.randrange(fm.per_lane)
+        ld = rnd.choice([fm.cols, fm.cols + 1, 4096, 4160, (1 << 40) + 7])
+        row0 = rnd.choice([0, 1, 17, 4095, (1 << 22), (1 << 62) // ld])
+        col0 = rnd.choice([0, 1, ld - fm.cols, max(0, ld - 1)])
+        assert lib.acc_matrix_offset(shape, lane, j, row0, col0, ld) == OL.matrix_offset(fm, lane, j, row0, col0, ld)
+
+
+def test_layout_argument_errors(lib):
+    for bad in [(2, 0, 0), (-1, 0, 0), (0, 64, 0), (0, -1, 0), (0, 0, 4), (1, 0, 16)]:
+        with pytest.raises(lib.MflError) as e:
+            lib.acc_coords(*bad)
+        assert e.value.status == lib.EINVAL
+    with pytest.raises(lib.MflError):
+        lib.acc_decode(0, 256)
+    with pytest.raises(lib.MflError):
+        lib.acc_decode(1, -1)
+    with pytest.raises(lib.MflError):
+        lib.acc_matrix_offset(0, 0, 0, -1, 0, 16)
+    with pytest.raises(lib.MflError):
+        lib.acc_matrix_offset(0, 0, 0, 0, 0, 0)
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null value; never dereferenced (rejected first)
+
+
+@pytest.mark.parametrize("call,status", [
+    # bad dtype / shape / orders / accumulate flag
+    (lambda m: m.gemm_tile_mma(7, 64, 64, 64, FAKE, 64, 0, FAKE, 64, 1, FAKE, 64), -1),
+    (lambda m: m.gemm_tile_mma_shape(2, 1, 64, 64, 64, FAKE, 64, 0, FAKE, 64, 1, FAKE, 64), -1),
+    (lambda m: m.gemm_tile_mma(1, 64, 64, 64, FAKE, 64, 3, FAKE, 64, 1, FAKE, 64), -1),
+    (lambda m: m.gemm_tile_mma(1, 64, 64, 64, FAKE, 64, 0, FAKE, 64, 1, FAKE, 64, accumulate=2), -1),
+    # null operands, misaligned pointer, ld too small, ld not a multiple of 8, negative sizes
+    (lambda m: m.gemm_tile_mma(1, 64, 64, 64, 0, 64, 0, FAKE, 64, 1, FAKE, 64), -1),
+    (lambda m: m.gemm_tile_mma(1, 64, 64, 64, FAKE + 2, 64, 0, FAKE, 64, 1, FAKE, 64), -1),
+    (lambda m: m.gemm_tile_mma(1, 64, 64, 64, FAKE, 56, 0, FAKE, 64, 1, FAKE, 64), -1),
+    (lambda m: m.gemm_tile_mma(1, 64, 64, 64, FAKE, 68, 0, FAKE, 64, 1, FAKE, 64), -1),
+    (lambda m: m.gemm_tile_mma(1, 64, 64, 64, FAKE, 64, 0, FAKE, 64, 1, FAKE, 32), -1),
+    (lambda m: m.gemm_tile_mma(1, -1, 64, 64, FAKE, 64, 0, FAKE, 64, 1, FAKE, 64), -1),
+    (lambda m: m.gemm_tile_mma(1, 64, 64, 64, FAKE, 64, 0, FAKE, 64, 1, 0, 64), -1),
+    (lambda m: m.gemm_tile_mma(1, 1 << 31, 64, 64, FAKE, 64, 0, FAKE, 64, 1, FAKE, 64), -3),
+    # block repeat: unsupported tile, non-multiple output
+    (lambda m: m.gemm_block_repeat(0, 48, 48, 64, 128, 64, 2048, 2048, FAKE, FAKE, FAKE), -3),
+    (lambda m: m.gemm_block_repeat(0, 64, 64, 64, 96, 64, 2048, 2048, FAKE, FAKE, FAKE), -3),
+    (lambda m: m.gemm_block_repeat(0, 64, 64, 64, 128, 64, 2000, 2048, FAKE, FAKE, FAKE), -3),
+    (lambda m: m.gemm_block_repeat(0, 64, 64, 64, 128, -1, 2048, 2048, FAKE, FAKE, FAKE), -1),
+    # split: chains beyond the products, lo*lo without two split operands, bad mode, ld % 4
+    (lambda m: m.gemm_split_fp32(1, 64, 64, 64, FAKE, 64, 0, 1, FAKE, 64, 1, 0, 3, 0, FAKE, 64), -1),
+    (lambda m: m.gemm_split_fp32(1, 64, 64, 64, FAKE, 64, 0, 1, FAKE, 64, 1, 0, 1, 1, FAKE, 64), -1),
+    (lambda m: m.gemm_split_fp32(1, 64, 64, 64, FAKE, 64, 0, 2, FAKE, 64, 1, 0, 1, 0, FAKE, 64), -1),
+    (lambda m: m.gemm_split_fp32(1, 64, 64, 64, FAKE, 66, 0, 1, FAKE, 64, 1, 1, 3, 0, FAKE, 64), -1),
+    (lambda m: m.gemm_split_fp32(1, 64, 64, 64, FAKE, 64, 0, 1, FAKE, 64, 1, 1, 0, 0, FAKE, 64), -1),
+    # attention: unsupported sizes, bad chains, small workspace, misaligned workspace
+    (lambda m: m.attention_split_fp32(2048, 32768, 64, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1 << 40), -3),
+    (lambda m: m.attention_split_fp32(2000, 32768, 128, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1 << 40), -3),
+    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 3, FAKE, FAKE, 1 << 40), -1),
+    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1024), -1),
+    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, FAKE, FAKE + 16, 1 << 40), -1),
+    # quantise / split: misaligned, negative n, bad dtype
+    (lambda m: m.quantize_fp32(1, FAKE + 4, FAKE, 16), -1),
+    (lambda m: m.quantize_fp32(1, FAKE, FAKE, -1), -1),
+    (lambda m: m.split_fp32(3, FAKE, FAKE, FAKE, 16), -1),
+    # strided store: spill past ldc, probe: bad shape
+    (lambda m: m.acc_store_strided(0, FAKE, FAKE, 0, 8, 16), -2),
+    (lambda m: m.acc_store_strided(1, FAKE, FAKE, (1 << 62), 0, 64), -2),
+    (lambda m: m.mfma_probe(2, 0, FAKE, FAKE, FAKE), -1),
+])
+def test_device_entry_points_reject_bad_arguments(lib, call, status):
+    with pytest.raises(lib.MflError) as e:
+        call(lib)
+    assert e.value.status == status
+
+
+def test_empty_problems_are_noops_without_a_device(lib):
+    # M = 0 or N = 0: nothing to do, no HIP call
+    lib.gemm_tile_mma(1, 0, 64, 64, FAKE, 64, 0, FAKE, 64, 1, FAKE, 64)
+    lib.gemm_tile_mma(1, 64, 0, 64, FAKE, 64, 0, FAKE, 64, 1, FAKE, 64)
+    lib.gemm_split_fp32(1, 0, 64, 64, FAKE, 64, 0, 1, FAKE, 64, 1, 1, 3, 0, FAKE, 64)
+    lib.gemm_block_repeat(0, 64, 64, 64, 128, 64, 0, 0, FAKE, FAKE, FAKE)
+    lib.quantize_fp32(1, FAKE, FAKE, 0)
+
+
+def test_attention_workspace_size(lib):
+    b = lib.attention_workspace_bytes(2048, 32768, 128)
+    assert b >= 2048 * 32768 * 4 + 2 * 2048 * 4 + 2048 * 128 * 4
+    with pytest.raises(lib.MflError):
+        lib.attention_workspace_bytes(2048, 32768, 96)

@@ -1,0 +1,58 @@
+"""attention_split_fp32 against the oracle: fp64 softmax(Q Q16(K)^T) Q16(V)
+with Q at its original values; normwise error <= 5e-6.  Small sizes in full,
+the 2048 x 32768 x 128 workload on sampled query rows."""
+import numpy as np
+import pytest
+import torch
+
+import mma_fragment_layouts_amd as mfl
+from mma_fragment_layouts_amd import inputs
+from oracle import reference as R
+
+from _gpu import dev32, device, host, say, stream
+
+pytestmark = pytest.mark.gpu
+
+
+def run_attention(q, k, v, chains):
+    nq, d = q.shape
+    nk = k.shape[0]
+    ws_bytes = mfl.attention_workspace_bytes(nq, nk, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device())
+    o = torch.full((nq, d), np.nan, device=device())
+    mfl.attention_split_fp32(nq, nk, d, dev32(q), dev32(k), dev32(v), chains, o, ws, ws_bytes, stream())
+    return host(o)
+
+
+@pytest.mark.parametrize("chains", [1, 2])
+@pytest.mark.parametrize("nq,nk", [(128, 128), (256, 1024), (384, 4096)])
+def test_attention_small(nq, nk, chains):
+    q, k, v = inputs.attention(nq, nk)
+    say("attention", nq, nk, chains)
+    o = run_attention(q, k, v, chains)
+    err = R.rel_error(o, R.attention_ref(q, k, v))
+    print(f"attention {nq}x{nk} chains={chains} err={err:.3e}")
+    assert err <= 5e-6
+
+
+def test_attention_uniform_closed_form():
+    """Q = 0: every score is 0, P is uniform and O is the column mean of Q16(V)."""
+    _, k, v = inputs.attention(128, 2048)
+    q = np.zeros((128, 128), np.float32)
+    say("attention Q=0")
+    o = run_attention(q, k, v, 2)
+    assert R.rel_error(o, R.attention_ref(q, k, v)) <= 5e-6
+
+
+def test_attention_full_size_sampled():
+    q, k, v = inputs.attention()
+    errs = {}
+    rows = np.random.default_rng(15).choice(2048, 64, replace=False)
+    ref = R.attention_ref(q[rows], k, v)
+    for chains in (1, 2):
+        say("attention 2048x32768", chains)
+        o = run_attention(q, k, v, chains)
+        assert not np.isnan(o).any()
+        errs[chains] = R.rel_error(o[rows], ref)
+    print("attention full-size errors", errs)
+    assert errs[2] <= 5e-6

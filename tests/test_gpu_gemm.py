@@ -1,0 +1,161 @@
+"""gemm_tile_mma against the oracle: fp64 product of the quantised inputs,
+normwise relative error <= 1e-5; bit-exact on integer-valued inputs; all four
+operand orders; ragged edges; NaN padding never read; the 4096^3 bf16 case in
+the launch configuration the benchmark times (sampled rows and entries)."""
+import numpy as np
+import pytest
+import torch
+
+import mma_fragment_layouts_amd as mfl
+from mma_fragment_layouts_amd import inputs
+from oracle import reference as R
+
+from _gpu import DT, dev32, device, host, q16, say, stream
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def storage(x_logical, order, ld, pad_value=np.nan):
+    """Storage array of a logical matrix in the given order and leading dim."""
+    if order == mfl.ROW_MAJOR:
+        rows, cols = x_logical.shape
+        s = np.full((rows, ld), pad_value, np.float32)
+        s[:, :cols] = x_logical
+    else:
+        cols, rows = x_logical.shape[1], x_logical.shape[0]
+        s = np.full((cols, ld), pad_value, np.float32)
+        s[:, :rows] = x_logical.T
+    return s
+
+
+def run_gemm(fmt, a, b, order_a=mfl.ROW_MAJOR, order_b=mfl.COL_MAJOR, pad=8, shape=None, accumulate=0, c0=None):
+    """a: logical M x K, b: logical K x N (fp32 numpy).  Returns C (numpy)."""
+    m, k = a.shape
+    n = b.shape[1]
+    lda = (k if order_a == mfl.ROW_MAJOR else m) + pad
+    ldb = (n if order_b == mfl.ROW_MAJOR else k) + pad
+    lda += (-lda) % 8
+    ldb += (-ldb) % 8
+    sa = storage(a, order_a, lda)
+    sb = storage(b, order_b, ldb)
+    da, db = q16(sa, fmt), q16(sb, fmt)
+    c = dev32(c0) if c0 is not None else torch.full((m, n), np.nan, device=device())
+    if shape is None:
+        mfl.gemm_tile_mma(DT[fmt], m, n, k, da, lda, order_a, db, ldb, order_b, c, n, accumulate, stream())
+    else:
+        mfl.gemm_tile_mma_shape(shape, DT[fmt], m, n, k, da, lda, order_a, db, ldb, order_b, c, n, accumulate,
+                                stream())
+    return host(c)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_gemm_small_config(fmt):
+    """M = N = K = 256, uniform[-1, 1], A row-major, B column-major."""
+    a, bt = inputs.gemm_small()
+    assert not np.array_equal(a, bt)
+    say("gemm 256^3", fmt)
+    c = run_gemm(fmt, a, bt.T)
+    assert R.rel_error(c, R.gemm_ref(a, bt, fmt)) <= TOL
+
+
+@pytest.mark.parametrize("oa", [mfl.ROW_MAJOR, mfl.COL_MAJOR])
+@pytest.mark.parametrize("ob", [mfl.ROW_MAJOR, mfl.COL_MAJOR])
+def test_all_operand_orders(oa, ob):
+    a, bt = inputs.gemm_small()
+    say("gemm orders", oa, ob)
+    c = run_gemm("f16", a, bt.T, oa, ob)
+    assert R.rel_error(c, R.gemm_ref(a, bt, "f16")) <= TOL
+
+
+def test_wrong_declared_order_gives_a_different_product():
+    """Declaring the wrong layout computes another product without any
+    out-of-bounds access (explainer, paragraph on leading dimensions)."""
+    a, bt = inputs.gemm_small()
+    c = run_gemm("f16", a, bt.T)
+    sa = storage(a, mfl.ROW_MAJOR, 256)
+    sb = storage(bt.T, mfl.COL_MAJOR, 256)
+    cc = torch.empty((256, 256), device=device())
+    mfl.gemm_tile_mma(mfl.F16, 256, 256, 256, q16(sa, "f16"), 256, mfl.COL_MAJOR, q16(sb, "f16"), 256,
+                      mfl.COL_MAJOR, cc, 256, 0, stream())
+    assert R.rel_error(host(cc), c) > 0.5
+
+
+@pytest.mark.parametrize("mnk", [(200, 136, 100), (129, 257, 72), (1, 1, 1), (17, 300, 8), (384, 384, 1000),
+                                 (256, 512, 130)])
+@pytest.mark.parametrize("orders", [(0, 1), (1, 0)])
+def test_ragged_sizes(mnk, orders):
+    m, n, k = mnk
+    rng = np.random.default_rng(m * 7 + n * 3 + k)
+    a = rng.uniform(-1, 1, (m, k)).astype(np.float32)
+    b = rng.uniform(-1, 1, (k, n)).astype(np.float32)
+    say("gemm ragged", mnk, orders)
+    c = run_gemm("bf16", a, b, *orders)
+    assert not np.isnan(c).any()
+    assert R.rel_error(c, R.gemm_ref(a, b.T, "bf16")) <= TOL
+
+
+def test_integer_inputs_are_bit_exact():
+    rng = np.random.default_rng(9)
+    m, n, k = 512, 512, 512
+    a = rng.integers(-16, 17, (m, k)).astype(np.float32)
+    b = rng.integers(-16, 17, (k, n)).astype(np.float32)
+    exact = a.astype(np.int64) @ b.astype(np.int64)
+    for shape in (0, 1):
+        say("gemm integer exact", shape)
+        c = run_gemm("bf16", a, b, shape=shape)
+        assert np.array_equal(c, exact.astype(np.float32))
+
+
+def test_accumulate_and_k_zero():
+    rng = np.random.default_rng(10)
+    a = rng.uniform(-1, 1, (256, 192)).astype(np.float32)
+    b = rng.uniform(-1, 1, (192, 320)).astype(np.float32)
+    c0 = rng.uniform(-1, 1, (256, 320)).astype(np.float32)
+    say("gemm accumulate")
+    c = run_gemm("f16", a, b, accumulate=1, c0=c0)
+    assert R.rel_error(c, c0 + R.gemm_ref(a, b.T, "f16")) <= TOL
+    say("gemm K = 0")
+    z = torch.full((64, 64), 3.0, device=device())
+    mfl.gemm_tile_mma(mfl.F16, 64, 64, 0, 0, 8, 0, 0, 8, 1, z, 64, 0, stream())
+    assert np.all(host(z) == 0)
+    mfl.gemm_tile_mma(mfl.F16, 64, 64, 0, 0, 8, 0, 0, 8, 1, z, 64, 1, stream())
+    assert np.all(host(z) == 0)
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+def test_fast_path_padded_nan(shape):
+    """Fast path (256-multiples, K-contiguous) with NaN in the padding of both
+    operands: a single read of the padding would poison the output."""
+    a, bt = inputs.gemm_dense(512, 768, 1024, pad=64)
+    say("fast path nan pad", shape)
+    c = torch.full((512, 768), np.nan, device=device())
+    mfl.gemm_tile_mma_shape(shape, mfl.BF16, 512, 768, 1024, q16(a, "bf16"), 1088, mfl.ROW_MAJOR, q16(bt, "bf16"),
+                            1088, mfl.COL_MAJOR, c, 768, 0, stream())
+    ch = host(c)
+    assert not np.isnan(ch).any()
+    assert R.rel_error(ch, R.gemm_ref(a[:, :1024], bt[:, :1024], "bf16")) <= TOL
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+def test_dense_4096_bf16_sampled(shape):
+    """The 4096^3 bf16 GEMM exactly as the benchmark launches it (A row-major,
+    B column-major, ld 4160 with NaN padding, C fp32 ldc 4096): no NaN anywhere,
+    48 full rows within 1e-5 normwise, and 4096 sampled entries elementwise."""
+    a, bt = inputs.gemm_dense()
+    say("dense 4096^3", shape)
+    c = torch.full((4096, 4096), np.nan, device=device())
+    mfl.gemm_tile_mma_shape(shape, mfl.BF16, 4096, 4096, 4096, q16(a, "bf16"), 4160, mfl.ROW_MAJOR,
+                            q16(bt, "bf16"), 4160, mfl.COL_MAJOR, c, 4096, 0, stream())
+    ch = host(c)
+    assert not np.isnan(ch).any()
+    rng = np.random.default_rng(11)
+    rows = rng.choice(4096, 48, replace=False)
+    ref_rows = R.gemm_ref(a[rows, :4096], bt[:, :4096], "bf16")
+    assert R.rel_error(ch[rows], ref_rows) <= TOL
+    r = rng.integers(0, 4096, 4096)
+    cc = rng.integers(0, 4096, 4096)
+    ref = R.gemm_ref_entries(a[:, :4096], bt[:, :4096], "bf16", r, cc)
+    # elementwise: fp32 accumulation of 4096 products, bound ~ K * u32 * sum|a||b|
+    scale = np.abs(ref).max()
+    assert np.max(np.abs(ch[r, cc] - ref)) <= 4096 * 2.0 ** -24 * 64 * max(scale, 1.0)

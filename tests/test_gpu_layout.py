@@ -1,0 +1,135 @@
+"""Device checks of the accumulator layouts against the hardware (cuda-oxide PR
+#474, "Verified against hardware"): one raw MFMA per instruction and operand
+type, operands gathered on the host, registers compared through the oracle's
+enumerated layout.  Expected values are exact integers computed on the host."""
+import numpy as np
+import pytest
+import torch
+
+import mma_fragment_layouts_amd as mfl
+from oracle import layouts as OL
+
+from _gpu import DT, device, host, say, stream
+
+pytestmark = pytest.mark.gpu
+
+GEOM = {0: (OL.MFMA_16X16X32, 16, 32), 1: (OL.MFMA_32X32X16, 32, 16)}  # map, MN, K
+
+
+def gather(a, b, mn):
+    """Operand fragments: lane l holds A[l % mn][8*(l // mn) + i] and
+    B[8*(l // mn) + i][l % mn], i = 0..7 (the CDNA4 operand layout of these
+    instructions)."""
+    af = np.zeros((64, 8), np.float32)
+    bf = np.zeros((64, 8), np.float32)
+    for l in range(64):
+        for i in range(8):
+            af[l, i] = a[l % mn, 8 * (l // mn) + i]
+            bf[l, i] = b[8 * (l // mn) + i, l % mn]
+    return af, bf
+
+
+def run_probe(shape, fmt, a, b):
+    fm, mn, k = GEOM[shape]
+    af, bf = gather(a, b, mn)
+    dev = device()
+    at = torch.from_numpy(af.reshape(-1)).to(dev)
+    bt = torch.from_numpy(bf.reshape(-1)).to(dev)
+    a16 = torch.empty(64 * 8, dtype=torch.int16, device=dev)
+    b16 = torch.empty(64 * 8, dtype=torch.int16, device=dev)
+    mfl.quantize_fp32(DT[fmt], at, a16, 64 * 8, stream())
+    mfl.quantize_fp32(DT[fmt], bt, b16, 64 * 8, stream())
+    acc = torch.full((64 * fm.per_lane,), float("nan"), device=dev)
+    mfl.mfma_probe(shape, DT[fmt], a16, b16, acc, stream())
+    return host(acc).reshape(64, fm.per_lane)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [0, 1])
+def test_identity_decode(shape, fmt):
+    """B = identity on a window of columns, A encodes its row (or column) index:
+    each register then names the output position it holds."""
+    fm, mn, k = GEOM[shape]
+    kw = min(k, mn)
+    mism = 0
+    for h in range(mn // kw):
+        for enc in ("row", "col"):
+            say("identity decode", shape, fmt, h, enc)
+            a = np.zeros((mn, k), np.float32)
+            b = np.zeros((k, mn), np.float32)
+            for r in range(mn):
+                for kk in range(kw):
+                    a[r, kk] = r + 1 if enc == "row" else kk + 1
+            for kk in range(kw):
+                b[kk, h * kw + kk] = 1.0
+            acc = run_probe(shape, fmt, a, b)
+            for l in range(64):
+                for j in range(fm.per_lane):
+                    r, c = fm.coords(l, j)
+                    inwin = h * kw <= c < (h + 1) * kw
+                    want = (r + 1 if enc == "row" else c - h * kw + 1) if inwin else 0.0
+                    mism += acc[l, j] != want
+    assert mism == 0, f"{mism} mismatched registers"
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [0, 1])
+def test_asymmetric_integer_matmul(shape, fmt):
+    """Distinct integers +-1..+-256 in A and a different arrangement in B: every
+    partial sum is an exact fp32 integer, so the product is bit-exact under any
+    accumulation order; a transposed or half-swapped layout cannot match."""
+    fm, mn, k = GEOM[shape]
+    rng = np.random.default_rng(100 + shape)
+    pool = np.array([v for v in range(-256, 257) if v != 0], np.float32)
+    a = rng.permutation(pool)[: mn * k].reshape(mn, k)
+    b = rng.permutation(pool)[: k * mn].reshape(k, mn)
+    assert not np.array_equal(a, b.T)
+    exact = (a.astype(np.int64) @ b.astype(np.int64)).astype(np.float64)
+    say("asymmetric matmul", shape, fmt)
+    acc = run_probe(shape, fmt, a, b)
+    mism, worst = 0, 0.0
+    for l in range(64):
+        for j in range(fm.per_lane):
+            r, c = fm.coords(l, j)
+            d = abs(float(acc[l, j]) - exact[r, c])
+            mism += d != 0
+            worst = max(worst, d)
+    assert (mism, worst) == (0, 0.0), f"{mism}/{64 * fm.per_lane} mismatched, worst abs diff {worst}"
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+def test_probe_scattered_by_strided_store_matches_host_matmul(shape):
+    """The page's flow end to end on the device: one MFMA, its registers
+    scattered into a padded matrix by the library's strided epilogue store, the
+    matrix compared with a host matmul; untouched elements stay untouched."""
+    fm, mn, k = GEOM[shape]
+    rng = np.random.default_rng(200 + shape)
+    a = rng.integers(-100, 100, (mn, k)).astype(np.float32)
+    b = rng.integers(-100, 100, (k, mn)).astype(np.float32)
+    exact = a.astype(np.float64) @ b.astype(np.float64)
+    say("probe + strided store", shape)
+    acc = torch.from_numpy(run_probe(shape, "f16", a, b).reshape(-1).copy()).to(device())
+    ld, row0, col0 = 3 * mn + 8, 5, mn + 3
+    c = torch.full((2 * mn + 7, ld), -7.0, device=device())
+    mfl.acc_store_strided(shape, acc, c, row0, col0, ld, stream())
+    ch = host(c)
+    want = np.full(ch.shape, -7.0)
+    want[row0:row0 + mn, col0:col0 + mn] = exact
+    assert np.array_equal(ch, want)
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+def test_strided_store_positions(shape):
+    fm, mn, _ = GEOM[shape]
+    vals = np.arange(64 * fm.per_lane, dtype=np.float32)   # acc[lane*J + j] = lane*J + j
+    acc = torch.from_numpy(vals).to(device())
+    ld, row0, col0 = 2 * mn + 3, 9, 2
+    c = torch.full((row0 + mn + 1, ld), -1.0, device=device())
+    say("strided store", shape)
+    mfl.acc_store_strided(shape, acc, c, row0, col0, ld, stream())
+    flat = host(c).reshape(-1)
+    want = np.full(flat.shape, -1.0)
+    for l in range(64):
+        for j in range(fm.per_lane):
+            want[OL.matrix_offset(fm, l, j, row0, col0, ld)] = l * fm.per_lane + j
+    assert np.array_equal(flat, want)
