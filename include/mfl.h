@@ -113,14 +113,15 @@ MFL_API int acc_store_strided(int shape, const float *acc, float *c, int64_t row
                       int64_t ldc, void *stream);
 
 /* Single-instruction probe (device): one wave executes one MFMA of `shape` and
- * `dtype` (MFL_F16 or MFL_BF16) with zero accumulator input.  a_frag and b_frag
- * hold each lane's 8 16-bit operand values lane-major (lane*8 + i); the raw
- * accumulator registers are written lane-major to acc (lane*J + j).  No layout
- * logic runs on the device: the caller gathers the operands and scatters the
- * result, which is how the layout is checked against hardware (cuda-oxide PR
- * #474, "Verified against hardware"). */
-MFL_API int mfma_probe(int shape, int dtype, const void *a_frag, const void *b_frag, float *acc,
-               void *stream);
+ * `dtype` (MFL_F16 or MFL_BF16).  a_frag and b_frag hold each lane's 8 16-bit
+ * operand values lane-major (lane*8 + i); c_in holds the accumulator input
+ * lane-major (lane*J + j), or is NULL for zeros; the raw accumulator registers
+ * are written lane-major to acc (lane*J + j).  No layout logic runs on the
+ * device: the caller gathers the operands and scatters the result, which is how
+ * the layout is checked against hardware (cuda-oxide PR #474, "Verified against
+ * hardware"), and how the rounding of the accumulation is measured. */
+MFL_API int mfma_probe(int shape, int dtype, const void *a_frag, const void *b_frag, const float *c_in,
+                       float *acc, void *stream);
 
 /* Round n fp32 values to `dtype` (round-to-nearest-even; NaN stays NaN,
  * overflow gives +-inf).  out receives n 16-bit values.  Tensor-core layout

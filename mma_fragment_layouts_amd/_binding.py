@@ -34,7 +34,7 @@ _SIGNATURES = {
     "acc_decode": (_i32, [_i32, _i32, _pi32, _pi32]),
     "acc_matrix_offset": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _pi64]),
     "acc_store_strided": (_i32, [_i32, _vp, _vp, _i64, _i64, _i64, _vp]),
-    "mfma_probe": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp]),
+    "mfma_probe": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "quantize_fp32": (_i32, [_i32, _vp, _vp, _i64, _vp]),
     "split_fp32": (_i32, [_i32, _vp, _vp, _vp, _i64, _vp]),
     "gemm_tile_mma": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _vp, _i64, _i32, _vp]),
@@ -153,8 +153,9 @@ def acc_store_strided(shape, acc, c, row0, col0, ldc, stream=None) -> None:
            "acc_store_strided")
 
 
-def mfma_probe(shape, dtype, a_frag, b_frag, acc, stream=None) -> None:
-    _check(load().mfma_probe(shape, dtype, _ptr(a_frag), _ptr(b_frag), _ptr(acc), _stream(stream)), "mfma_probe")
+def mfma_probe(shape, dtype, a_frag, b_frag, c_in, acc, stream=None) -> None:
+    _check(load().mfma_probe(shape, dtype, _ptr(a_frag), _ptr(b_frag), _ptr(c_in), _ptr(acc), _stream(stream)),
+           "mfma_probe")
 
 
 def quantize_fp32(dtype, x, out, n, stream=None) -> None:

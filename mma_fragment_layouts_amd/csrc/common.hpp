@@ -73,12 +73,22 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (ui
 // cycle.  Because the swizzle repeats every 16 rows, fragment i of a wave sits
 // a fixed i*16*BK elements after fragment 0 (an immediate offset).
 template <int BK>
-__device__ __forceinline__ int swz(int row) {
+MFL_HD constexpr int swz(int row) {
   if constexpr (BK == 64)
     return ((row & 7) ^ ((row >> 3) & 1)) & 7;
   else
-    return ((row >> 1) ^ (row >> 3)) & 3;  // BK == 32
+    return ((row >> 1) ^ ((row >> 3) & 1)) & 3;  // BK == 32: bits 1-3 of the row only
 }
+// The fragment addressing (immediate i*16*BK offsets) needs the swizzle to
+// repeat every 16 rows.
+template <int BK>
+constexpr bool swz_period16() {
+  for (int r = 0; r < 1024; ++r)
+    if (swz<BK>(r) != swz<BK>(r & 15)) return false;
+  return true;
+}
+static_assert(swz_period16<64>() && swz_period16<32>(), "LDS swizzle must depend on row mod 16 only");
+
 // Element offset (in 16-bit units) of chunk `chunk` of row `row`.
 template <int BK>
 __device__ __forceinline__ int lds_chunk(int row, int chunk) {

@@ -178,9 +178,11 @@ __device__ __forceinline__ void store_acc_rsrc(rsrc_t c, uint32_t ldc, int lane,
       const uint32_t srow = (uint32_t)(i * MN + acc_row(L, 0, v)) * ldc * 4u;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
+        // the b32 buffer builtins move raw 32-bit patterns: bit-cast, never convert
         float x = acc[i][j][v];
-        if constexpr (ACCUM) x += __builtin_amdgcn_raw_buffer_load_b32(c, voff + j * MN * 4, srow, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(x, c, voff + j * MN * 4, srow, 0);
+        if constexpr (ACCUM)
+          x += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(c, voff + j * MN * 4, srow, 0));
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), c, voff + j * MN * 4, srow, 0);
       }
     }
 }

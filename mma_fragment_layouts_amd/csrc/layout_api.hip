@@ -31,13 +31,13 @@ __global__ __launch_bounds__(64) void acc_store_kernel(const float* __restrict__
 // One wave, one MFMA, zero accumulator in; raw registers out lane-major.
 template <int SHAPE, int DT>
 __global__ __launch_bounds__(64) void mfma_probe_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
-                                                       float* __restrict__ out) {
+                                                       const float* __restrict__ c_in, float* __restrict__ out) {
   const int lane = threadIdx.x;
   const u32x4 av = *reinterpret_cast<const u32x4*>(a + lane * 8);
   const u32x4 bv = *reinterpret_cast<const u32x4*>(b + lane * 8);
   typename Shape<SHAPE>::Acc c;
 #pragma unroll
-  for (int j = 0; j < Shape<SHAPE>::J; ++j) c[j] = 0.f;
+  for (int j = 0; j < Shape<SHAPE>::J; ++j) c[j] = c_in ? c_in[lane * Shape<SHAPE>::J + j] : 0.f;
   c = mfma<SHAPE, DT>(av, bv, c);
 #pragma unroll
   for (int j = 0; j < Shape<SHAPE>::J; ++j) out[lane * Shape<SHAPE>::J + j] = c[j];
@@ -122,19 +122,20 @@ extern "C" int acc_store_strided(int shape, const float* acc, float* c, int64_t 
   return launch_status();
 }
 
-extern "C" int mfma_probe(int shape, int dtype, const void* a_frag, const void* b_frag, float* acc, void* stream) {
+extern "C" int mfma_probe(int shape, int dtype, const void* a_frag, const void* b_frag, const float* c_in, float* acc,
+                          void* stream) {
   if (!valid_shape(shape) || (dtype != MFL_F16 && dtype != MFL_BF16)) return MFL_EINVAL;
   if (!a_frag || !b_frag || !acc || !aligned16(a_frag) || !aligned16(b_frag)) return MFL_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   const uint16_t* a = (const uint16_t*)a_frag;
   const uint16_t* b = (const uint16_t*)b_frag;
   if (shape == MFL_MFMA_16X16X32 && dtype == MFL_BF16)
-    hipLaunchKernelGGL((mfma_probe_kernel<0, MFL_BF16>), dim3(1), dim3(64), 0, s, a, b, acc);
+    hipLaunchKernelGGL((mfma_probe_kernel<0, MFL_BF16>), dim3(1), dim3(64), 0, s, a, b, c_in, acc);
   else if (shape == MFL_MFMA_16X16X32)
-    hipLaunchKernelGGL((mfma_probe_kernel<0, MFL_F16>), dim3(1), dim3(64), 0, s, a, b, acc);
+    hipLaunchKernelGGL((mfma_probe_kernel<0, MFL_F16>), dim3(1), dim3(64), 0, s, a, b, c_in, acc);
   else if (dtype == MFL_BF16)
-    hipLaunchKernelGGL((mfma_probe_kernel<1, MFL_BF16>), dim3(1), dim3(64), 0, s, a, b, acc);
+    hipLaunchKernelGGL((mfma_probe_kernel<1, MFL_BF16>), dim3(1), dim3(64), 0, s, a, b, c_in, acc);
   else
-    hipLaunchKernelGGL((mfma_probe_kernel<1, MFL_F16>), dim3(1), dim3(64), 0, s, a, b, acc);
+    hipLaunchKernelGGL((mfma_probe_kernel<1, MFL_F16>), dim3(1), dim3(64), 0, s, a, b, c_in, acc);
   return launch_status();
 }

@@ -170,7 +170,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-null value; never dereferenced (rejected
     # strided store: spill past ldc, probe: bad shape
     (lambda m: m.acc_store_strided(0, FAKE, FAKE, 0, 8, 16), -2),
     (lambda m: m.acc_store_strided(1, FAKE, FAKE, (1 << 62), 0, 64), -2),
-    (lambda m: m.mfma_probe(2, 0, FAKE, FAKE, FAKE), -1),
+    (lambda m: m.mfma_probe(2, 0, FAKE, FAKE, None, FAKE), -1),
 ])
 def test_device_entry_points_reject_bad_arguments(lib, call, status):
     with pytest.raises(lib.MflError) as e:

@@ -29,7 +29,7 @@ def gather(a, b, mn):
     return af, bf
 
 
-def run_probe(shape, fmt, a, b):
+def run_probe(shape, fmt, a, b, c_in=None):
     fm, mn, k = GEOM[shape]
     af, bf = gather(a, b, mn)
     dev = device()
@@ -40,7 +40,14 @@ def run_probe(shape, fmt, a, b):
     mfl.quantize_fp32(DT[fmt], at, a16, 64 * 8, stream())
     mfl.quantize_fp32(DT[fmt], bt, b16, 64 * 8, stream())
     acc = torch.full((64 * fm.per_lane,), float("nan"), device=dev)
-    mfl.mfma_probe(shape, DT[fmt], a16, b16, acc, stream())
+    cin = None
+    if c_in is not None:   # c_in: logical mn x mn matrix, handed over lane-major through the oracle layout
+        lm = np.zeros((64, fm.per_lane), np.float32)
+        for l in range(64):
+            for j in range(fm.per_lane):
+                lm[l, j] = c_in[fm.coords(l, j)]
+        cin = torch.from_numpy(lm.reshape(-1)).to(dev)
+    mfl.mfma_probe(shape, DT[fmt], a16, b16, cin, acc, stream())
     return host(acc).reshape(64, fm.per_lane)
 
 
@@ -133,3 +140,55 @@ def test_strided_store_positions(shape):
         for j in range(fm.per_lane):
             want[OL.matrix_offset(fm, l, j, row0, col0, ld)] = l * fm.per_lane + j
     assert np.array_equal(flat, want)
+
+
+ULP1 = 2.0 ** -23      # fp32 spacing just above 1.0
+CASES = {
+    # name: (C[0][0], [(a_k, b_k) ...]) — every product exact in both 16-bit formats
+    "c=1 + 0.75ulp": (1.0, [(3 * 2.0 ** -12, 2.0 ** -13)]),
+    "c=1 + 3 x 0.375ulp": (1.0, [(3 * 2.0 ** -13, 2.0 ** -13)] * 3),
+    "c=0, 2^20 + 2^-20 - 2^20": (0.0, [(2.0 ** 10, 2.0 ** 10), (2.0 ** -10, 2.0 ** -10), (-(2.0 ** 10), 2.0 ** 10)]),
+    "c=2^24 + 1.5": (2.0 ** 24, [(1.5, 1.0)]),
+    "c=1 - 0.375ulp x 3": (1.0, [(-3 * 2.0 ** -13, 2.0 ** -13)] * 3),
+}
+# What each rounding model gives: exact products summed exactly, then one
+# rounding into fp32, to nearest-even (RN-once) or toward zero (RZ-once); and a
+# sequential fp32 sum in product order with either rounding (RN-seq, RZ-seq).
+M1 = 2.0 ** -24        # fp32 spacing just below 1.0
+MODELS = {
+    "c=1 + 0.75ulp": {"RN-once": 1 + ULP1, "RZ-once": 1.0, "RN-seq": 1 + ULP1, "RZ-seq": 1.0},
+    "c=1 + 3 x 0.375ulp": {"RN-once": 1 + ULP1, "RZ-once": 1 + ULP1, "RN-seq": 1.0, "RZ-seq": 1.0},
+    "c=0, 2^20 + 2^-20 - 2^20": {"RN-once": 2.0 ** -20, "RZ-once": 2.0 ** -20, "RN-seq": 0.0, "RZ-seq": 0.0},
+    "c=2^24 + 1.5": {"RN-once": 2.0 ** 24 + 2, "RZ-once": 2.0 ** 24, "RN-seq": 2.0 ** 24 + 2, "RZ-seq": 2.0 ** 24},
+    "c=1 - 0.375ulp x 3": {"RN-once": 1 - 2 * M1, "RZ-once": 1 - 3 * M1, "RN-seq": 1 - 3 * M1, "RZ-seq": 1 - 3 * M1},
+}
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [0, 1])
+def test_mfma_accumulation_rounding(shape, fmt):
+    """Measures how one MFMA rounds C + sum_k a_k b_k (the explainer warns that
+    instruction accumulation may differ from a sequential scalar sum; Strata PR
+    #800 describes truncation on another architecture).  Every case's result is
+    reported with the models it agrees with; the test requires each result to
+    match at least one model."""
+    fm, mn, k = GEOM[shape]
+    report = {}
+    for name, (c00, prods) in CASES.items():
+        a = np.zeros((mn, k), np.float32)
+        b = np.zeros((k, mn), np.float32)
+        for i, (x, y) in enumerate(prods):
+            a[0, i], b[i, 0] = x, y
+        c = np.zeros((mn, mn), np.float32)
+        c[0, 0] = c00
+        say("accumulation probe", shape, fmt, name)
+        acc = run_probe(shape, fmt, a, b, c)
+        got = None
+        for l in range(64):
+            for j in range(fm.per_lane):
+                if fm.coords(l, j) == (0, 0):
+                    got = float(acc[l, j])
+        models = [m for m, v in MODELS[name].items() if v == got]
+        report[name] = (got, models)
+        assert models, f"{name}: {got!r} matches no model"
+    print(f"mfma accumulation shape={shape} {fmt}:", report)
