@@ -58,6 +58,26 @@ def best_of(fn, stream, warm=3, rounds=3, per=20):
     return min(event_time_ms(fn, per, stream) for _ in range(rounds)) / per
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_4096_bf16_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    record (scaled by a plain copy), or None when the kernel sources have changed
+    since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return int(rec["read_bytes"] + rec["write_bytes"])
+    except Exception:
+        return None
+
+
 def cpu_baseline(a, bt):
     """The oracle as it stands (numpy fp64 on the quantised inputs), timed on the
     host's cores over the full 4096^3 problem."""
@@ -144,6 +164,8 @@ def main():
     p.add_argument("--shape", type=int, default=0, help="MFMA shape of the GEMM fast path (0: 16x16x32, 1: 32x32x16)")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run 3 plain device copies of 256 MiB (reference for the HBM byte counters)")
     args = p.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM shards by output "
@@ -215,11 +237,19 @@ def main():
         "config": {"workload": "dense GEMM M=N=K=4096, bf16 A row-major / B col-major, lda=ldb=4160 (NaN pad), "
                                "fp32 accumulate, fp32 C ldc=4096",
                    "m": M, "n": N, "k": K, "lda": LD, "ldb": LD, "ldc": N,
-                   "mfma": "16x16x32" if args.shape == 0 else "32x32x16", "tile": "256x256x64, 4 waves"},
+                   "mfma": "16x16x32" if args.shape == 0 else "32x32x16", "tile": "256x256x64, 16 waves (64x64 each)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
     }
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_extra:
         log("other workloads")
         result["workloads"] = extra_workloads(torch, mfl, inputs, stream)

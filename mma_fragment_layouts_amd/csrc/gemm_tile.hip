@@ -85,8 +85,20 @@ static int launch_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, f
 // with no staging registers.  The swizzle is applied on the source side: the
 // lane that lands in physical chunk p of row r fetches logical chunk p ^ swz(r).
 // Per-lane state is one 32-bit offset per operand; the row step of each load
-// instruction and the K step are uniform scalar offsets.
-template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT>
+// instruction and the K step are uniform scalar offsets.  Sixteen waves (four
+// per SIMD, 64 x 64 outputs each) let one wave's MFMAs run while another waits
+// on LDS or on the barrier; at 256 x 256 x 64 the ds_read_b128 fragment traffic
+// (4 LDS cycles each, conflict free) stays below the MFMA time.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// STAGES-deep ring of LDS stages: stage kt+STAGES-1 is requested while stage kt
+// feeds the MFMAs.  One barrier per K step both publishes stage kt (every
+// wave's loads for it have landed) and retires stage kt-1, whose buffer the
+// new request reuses.
+template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT, int STAGES>
 __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t* __restrict__ A,
                                                                    const uint16_t* __restrict__ B,
                                                                    float* __restrict__ C, uint32_t lda, uint32_t ldb,
@@ -99,11 +111,13 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
   constexpr int TM = WM / MN, TN = WN / MN;
   constexpr int STAGE = (BM + BN) * BK;
   constexpr int A_INSTR = BM / 8 / NW, B_INSTR = BN / 8 / NW;
+  constexpr int LOADS = A_INSTR + B_INSTR;
   static_assert(A_INSTR * 8 * NW == BM && B_INSTR * 8 * NW == BN, "tile rows must split into 8-row wave loads");
   static_assert((NW % 2) == 0, "per-lane swizzle is load-invariant only for an even number of waves");
+  static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "vmcnt range");
   using Acc = typename Shape<SHAPE>::Acc;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE];
 
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, &tm, &tn);
@@ -139,17 +153,20 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
   zero_acc<SHAPE, TM, TN>(acc);
 
   const int KT = K / BK;
-  if (KT > 0) {
-    issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < KT) issue(st, st * BK);
+  for (int kt = 0; kt < KT; ++kt) {
+    // this wave's loads for stage kt are done when at most the later stages'
+    // loads are still in flight; near the end fewer later stages exist
+    if (kt + STAGES - 2 < KT)
+      wait_vmcnt<(STAGES - 2) * LOADS>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) issue(cur ^ 1, (kt + 1) * BK);
-      mma_slab<SHAPE, DT, TM, TN, BK>(lds + cur * STAGE, lds + cur * STAGE + BM * BK, fa, fb, acc);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
+    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
+    const int cur = (kt % STAGES) * STAGE;
+    mma_slab<SHAPE, DT, TM, TN, BK>(lds + cur, lds + cur + BM * BK, fa, fb, acc);
   }
   // The store buffer starts at this wave's tile origin and spans its WM rows.
   const rsrc_t rc = make_rsrc(C + (int64_t)(row0 + wr0) * ldc + col0 + wc0, (uint32_t)WM * ldc * 4u);
@@ -159,11 +176,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
     store_acc_rsrc<SHAPE, TM, TN, false>(rc, ldc, lane, acc);
 }
 
-template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT>
+template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT, int STAGES = 2>
 static int launch_fast(const void* a, int64_t lda, const void* b, int64_t ldb, float* c, int64_t ldc, int M, int N,
                        int K, int accumulate, hipStream_t stream) {
   const int tiles_m = M / BM, tiles_n = N / BN;
-  hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WGM, WGN, SHAPE, DT>), dim3(tiles_m * tiles_n), dim3(WGM * WGN * 64), 0,
+  hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WGM, WGN, SHAPE, DT, STAGES>), dim3(tiles_m * tiles_n),
+                     dim3(WGM * WGN * 64), 0,
                      stream, (const uint16_t*)a, (const uint16_t*)b, c, (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, K,
                      tiles_m, tiles_n, accumulate);
   return launch_status();
@@ -190,9 +208,10 @@ static int dispatch(int shape, const void* a, int64_t lda, int oa, const void* b
                     int64_t ldc, int M, int N, int K, int accumulate, hipStream_t s) {
   const bool ak = oa == MFL_ROW_MAJOR, bk = ob == MFL_COL_MAJOR;
   if (ak && bk && M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && fast_fits(lda, ldb, ldc)) {
+    // 16 waves (4 per SIMD), 64 x 64 outputs per wave
     if (shape == MFL_MFMA_32X32X16)
-      return launch_fast<256, 256, 2, 2, 1, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-    return launch_fast<256, 256, 2, 2, 0, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+      return launch_fast<256, 256, 4, 4, 1, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+    return launch_fast<256, 256, 4, 4, 0, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
   }
   if (ak && bk) return launch_generic<DT, true, true>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
   if (ak) return launch_generic<DT, true, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
