@@ -111,7 +111,9 @@ def extra_workloads(torch, mfl, inputs, stream):
     da, db = q16(a, mfl.F16), q16(bt, mfl.F16)
     c = torch.empty((256, 256), device=dev)
     ms = best_of(lambda: mfl.gemm_tile_mma(mfl.F16, 256, 256, 256, da, 256, 0, db, 256, 1, c, 256, 0, stream), stream)
-    out["gemm_256_f16"] = {"us": round(ms * 1e3, 2), "tflops": round(2 * 256 ** 3 / ms / 1e9, 2)}
+    out["gemm_256_f16"] = {"us": round(ms * 1e3, 2), "tflops": round(2 * 256 ** 3 / ms / 1e9, 2),
+                           "bound": "latency (16 workgroups)",
+                           "frac_mfma_peak": round(2 * 256 ** 3 / ms / 1e9 / PEAK_BF16_TFLOPS, 5)}
 
     # block repeat, 2048^2 output, 64 repeats
     rep = {}
@@ -122,8 +124,9 @@ def extra_workloads(torch, mfl, inputs, stream):
             da, db = q16(a, dt), q16(bt, dt)
             c = torch.empty((2048, 2048), device=dev)
             ms = best_of(lambda: mfl.gemm_block_repeat(dt, tm, tn, tk, th, 64, 2048, 2048, da, db, c, stream), stream)
-            rep[f"{tm}x{tn}x{tk}/{th}/{name}"] = round(2 * 2048 * 2048 * tk * 64 / ms / 1e9, 1)
-    out["block_repeat_tflops"] = rep
+            tf = 2 * 2048 * 2048 * tk * 64 / ms / 1e9
+            rep[f"{tm}x{tn}x{tk}/{th}/{name}"] = {"tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    out["block_repeat"] = rep
 
     # split fp32 GEMM 4096^3, bf16 pieces
     a, bt = inputs.gemm_split()
@@ -135,23 +138,28 @@ def extra_workloads(torch, mfl, inputs, stream):
         ms = best_of(lambda: mfl.gemm_split_fp32(mfl.BF16, 4096, 4096, 4096, da, 4096, 0, 1, db, 4096, 1, 1, chains,
                                                  lolo, c, 4096, 0, stream), stream, rounds=2, per=5)
         nprod = 3 + lolo
+        mf = nprod * 2 * 4096 ** 3 / ms / 1e9
         sp[f"chains{chains}{'+lolo' if lolo else ''}"] = {
             "us": round(ms * 1e3, 1), "useful_tflops": round(2 * 4096 ** 3 / ms / 1e9, 1),
-            "mfma_tflops": round(nprod * 2 * 4096 ** 3 / ms / 1e9, 1)}
+            "mfma_tflops": round(mf, 1), "frac_mfma_peak": round(mf / PEAK_BF16_TFLOPS, 4)}
     out["split_4096"] = sp
     del da, db, c
 
     # attention pair 2048 x 32768 x 128
     q, k, v = inputs.attention()
     dq, dk, dv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
-    wsb = mfl.attention_workspace_bytes(2048, 32768, 128)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     o = torch.empty((2048, 128), device=dev)
     att = {}
-    for chains in (1, 2):
-        ms = best_of(lambda: mfl.attention_split_fp32(2048, 32768, 128, dq, dk, dv, chains, o, ws, wsb, stream),
-                     stream, rounds=2, per=5)
-        att[f"chains{chains}_ms"] = round(ms, 3)
+    for algo, aname in ((mfl.ATTN_MATERIALISED, "materialised"), (mfl.ATTN_FUSED, "fused")):
+        wsb = mfl.attention_workspace_bytes(2048, 32768, 128, algo)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        for chains in (1, 2):
+            ms = best_of(lambda: mfl.attention_split_fp32(2048, 32768, 128, dq, dk, dv, chains, algo, o, ws, wsb,
+                                                          stream), stream, rounds=2, per=5)
+            mf = 2 * 2 * 2 * 2048 * 32768 * 128 / ms / 1e9   # 2 GEMMs x 2 products (hi, lo)
+            att[f"{aname}_chains{chains}"] = {"ms": round(ms, 4), "mfma_tflops": round(mf, 1),
+                                              "frac_mfma_peak": round(mf / PEAK_BF16_TFLOPS, 4)}
+        del ws
     out["attention_2048x32768"] = att
     return out
 

@@ -182,8 +182,9 @@ MFL_API int gemm_tile_mma_shape(int shape, int dtype, int64_t m, int64_t n, int6
                                 const void *b, int64_t ldb, int order_b,
                                 float *c, int64_t ldc, int accumulate, void *stream);
 
-/* Bytes of device workspace attention_split_fp32 needs for these sizes. */
-MFL_API int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int64_t *bytes);
+/* Bytes of device workspace attention_split_fp32 needs for these sizes and
+ * `algo`. */
+MFL_API int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int algo, int64_t *bytes);
 
 /* Attention-shaped pair of split GEMMs, one head (Strata PR #800): q (nq x d),
  * k and v (nk x d), o (nq x d), all fp32 row-major with ld = d.
@@ -192,11 +193,16 @@ MFL_API int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int64_t
  *   O = (P~ V) / l with P~ split into f16 hi/lo and V rounded once to f16.
  * `chains` (1 or 2) selects single-chain or separate hi/lo accumulators for
  * both products.  No causal mask and no 1/sqrt(d) scaling are applied.
+ *   algo 0: the four steps as separate kernels, S and P~ materialised in the
+ *           workspace (split GEMM, row softmax, split-K split GEMM, reduce);
+ *   algo 1: fused — per 128 queries and key slice, both products and an online
+ *           softmax (running max, rescaled accumulators) stay in registers and
+ *           LDS; key slices are merged by their exp(m_s - m) weights.
  * Supported: d = 128, nq and nk multiples of 128.  `workspace` is device memory
- * of at least attention_workspace_bytes() bytes, 256-byte aligned. */
+ * of at least attention_workspace_bytes(..., algo) bytes, 256-byte aligned. */
 MFL_API int attention_split_fp32(int64_t nq, int64_t nk, int64_t d, const float *q, const float *k,
-                         const float *v, int chains, float *o, void *workspace,
-                         int64_t workspace_bytes, void *stream);
+                                 const float *v, int chains, int algo, float *o, void *workspace,
+                                 int64_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

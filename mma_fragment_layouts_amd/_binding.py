@@ -21,6 +21,7 @@ MFMA_16X16X32, MFMA_32X32X16 = 0, 1
 F16, BF16 = 0, 1
 ROW_MAJOR, COL_MAJOR = 0, 1
 ROUND, SPLIT = 0, 1
+ATTN_MATERIALISED, ATTN_FUSED = 0, 1
 
 _i32, _i64, _vp = C.c_int, C.c_int64, C.c_void_p
 _pi32, _pi64 = C.POINTER(C.c_int), C.POINTER(C.c_int64)
@@ -43,8 +44,8 @@ _SIGNATURES = {
     "gemm_block_repeat": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp]),
     "gemm_split_fp32": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _i64, _i32, _i32, _i32, _i32,
                                _vp, _i64, _i32, _vp]),
-    "attention_workspace_bytes": (_i32, [_i64, _i64, _i64, _pi64]),
-    "attention_split_fp32": (_i32, [_i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _vp]),
+    "attention_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _pi64]),
+    "attention_split_fp32": (_i32, [_i64, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i64, _vp]),
 }
 EXPORTS = tuple(_SIGNATURES)
 
@@ -188,12 +189,12 @@ def gemm_split_fp32(piece, m, n, k, a, lda, order_a, mode_a, b, ldb, order_b, mo
                                   chains, lolo, _ptr(c), ldc, accumulate, _stream(stream)), "gemm_split_fp32")
 
 
-def attention_workspace_bytes(nq, nk, d) -> int:
+def attention_workspace_bytes(nq, nk, d, algo=1) -> int:
     b = C.c_int64()
-    _check(load().attention_workspace_bytes(nq, nk, d, C.byref(b)), "attention_workspace_bytes")
+    _check(load().attention_workspace_bytes(nq, nk, d, algo, C.byref(b)), "attention_workspace_bytes")
     return b.value
 
 
-def attention_split_fp32(nq, nk, d, q, k, v, chains, o, workspace, workspace_bytes, stream=None) -> None:
-    _check(load().attention_split_fp32(nq, nk, d, _ptr(q), _ptr(k), _ptr(v), chains, _ptr(o), _ptr(workspace),
-                                       workspace_bytes, _stream(stream)), "attention_split_fp32")
+def attention_split_fp32(nq, nk, d, q, k, v, chains, algo, o, workspace, workspace_bytes, stream=None) -> None:
+    _check(load().attention_split_fp32(nq, nk, d, _ptr(q), _ptr(k), _ptr(v), chains, algo, _ptr(o),
+                                       _ptr(workspace), workspace_bytes, _stream(stream)), "attention_split_fp32")

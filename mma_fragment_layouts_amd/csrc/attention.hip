@@ -1,5 +1,6 @@
 // attention_split_fp32: the attention-shaped pair of split GEMMs of Strata PR
-// #800 ("What's going on": q is split for q.k, p is split for p.v, each into an
+// #800 — algo 0 (below) materialises the scores; algo 1 is the fused kernel of
+// attention_fused.hip ("What's going on": q is split for q.k, p is split for p.v, each into an
 // FP16 hi and lo half; "The fix": hi and lo products in separate accumulators).
 //
 //   1. S = Q K^T           split GEMM, Q split into f16 hi/lo, K rounded once
@@ -13,9 +14,15 @@
 // fp16's subnormal range and lose most of their lo half.  softmax(S) V equals
 // (P~ V) / l exactly in real arithmetic.  This version materialises S / P~ in
 // the caller's workspace (HBM-bound); it keeps every step on the device.
+#include "attention_fused.hpp"
 #include "gemm_split.hpp"
 
 namespace mfl {
+
+int64_t attn_fused_workspace(int64_t nq, int64_t nk);
+int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, const float* v, int chains, float* o,
+                      void* workspace, hipStream_t st);
+
 namespace {
 
 constexpr int kSoftmaxThreads = 256;
@@ -168,23 +175,29 @@ bool valid_sizes(int64_t nq, int64_t nk, int64_t d) {
 
 using namespace mfl;
 
-extern "C" int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int64_t* bytes) {
-  if (!bytes) return MFL_EINVAL;
+extern "C" int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int algo, int64_t* bytes) {
+  if (!bytes || (algo != 0 && algo != 1)) return MFL_EINVAL;
   if (!valid_sizes(nq, nk, d)) return MFL_EUNSUPPORTED;
-  *bytes = plan(nq, nk, d).total;
+  *bytes = algo == 0 ? plan(nq, nk, d).total : attn_fused_workspace(nq, nk);
   return MFL_OK;
 }
 
 extern "C" int attention_split_fp32(int64_t nq, int64_t nk, int64_t d, const float* q, const float* k, const float* v,
-                                    int chains, float* o, void* workspace, int64_t workspace_bytes, void* stream) {
+                                    int chains, int algo, float* o, void* workspace, int64_t workspace_bytes,
+                                    void* stream) {
   if (chains != 1 && chains != 2) return MFL_EINVAL;
+  if (algo != 0 && algo != 1) return MFL_EINVAL;
   if (!valid_sizes(nq, nk, d)) return nq < 0 || nk < 0 || d < 0 ? MFL_EINVAL : MFL_EUNSUPPORTED;
   if (!q || !k || !v || !o || !workspace) return MFL_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MFL_EINVAL;
   if (((uintptr_t)workspace & 255) != 0) return MFL_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (algo == 1) {
+    if (workspace_bytes < attn_fused_workspace(nq, nk)) return MFL_EINVAL;
+    return launch_attn_fused(nq, nk, q, k, v, chains, o, workspace, s);
+  }
   const Workspace w = plan(nq, nk, d);
   if (workspace_bytes < w.total) return MFL_EINVAL;
-  hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   float* S = (float*)(ws + w.s_off);
   float* m = (float*)(ws + w.m_off);

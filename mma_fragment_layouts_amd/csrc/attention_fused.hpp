@@ -1,0 +1,49 @@
+// Fused split-precision attention (one head, head dim 128): the kernel shape of
+// Strata PR #800 ("What's going on": q is split for q.k and p for p.v into an
+// FP16 hi and lo half; "The fix": the halves accumulate in separate chains that
+// are added in plain fp32), with the scores never leaving the compute unit.
+//
+// Work split: a workgroup owns 128 queries (4 waves x 32) and one slice of the
+// keys.  Per 64-key chunk:
+//   GEMM1  S^T (64 keys x 32 queries per wave) = K16 . Q^T, with Q's hi and lo
+//          halves as B fragments held in registers for the whole kernel (two
+//          chains, summed in fp32);
+//   online softmax on the accumulators: running max m per query (reduced across
+//          the four lanes that share a query), P~ = exp(S - m) in (0, 1], the
+//          output accumulators and the per-lane partial sum l rescaled by
+//          exp(m_old - m_new) when the max grows;
+//   GEMM2  O^T (128 dims x 32 queries) += V16^T . P~^T, with P~ split into fp16
+//          hi/lo B fragments built directly from the S^T accumulator registers
+//          (two chains).
+// Each slice writes its unnormalised O, m and l; a combine kernel merges the
+// slices with exp(m_s - max_s m_s) weights in a fixed order and divides by l.
+//
+// Layout trick: the S^T accumulator gives lane l (query l mod 16, group
+// g = l div 16) the keys 16*t' + 4g + j of each 16-key tile t'.  For GEMM2 the
+// lane's 8 K positions 8g..8g+7 of 32-key block t are taken to be keys
+// 32t + 4g + j (from tile 2t) and 32t + 16 + 4g + j (from tile 2t + 1); the
+// preparation pass stores V^T with the keys of every 32-key block permuted so
+// that exactly those 8 keys are contiguous — then the V^T fragment is one
+// 16-byte read like any other.
+#pragma once
+#include "gemm_core.hpp"
+
+namespace mfl {
+
+constexpr int kAttnQ = 128;   // queries per workgroup
+constexpr int kAttnKV = 64;   // keys per chunk
+constexpr int kAttnD = 128;   // head dimension
+
+// Storage position of key r (0..31) inside its 32-key block of V^T.
+MFL_HD constexpr int vt_key_pos(int r) { return 8 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3); }
+
+constexpr bool vt_perm_is_bijection() {
+  int seen[32] = {};
+  for (int r = 0; r < 32; ++r) seen[vt_key_pos(r)]++;
+  for (int p = 0; p < 32; ++p)
+    if (seen[p] != 1) return false;
+  return true;
+}
+static_assert(vt_perm_is_bijection(), "V^T key permutation must be a bijection");
+
+}  // namespace mfl

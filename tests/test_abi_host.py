@@ -158,11 +158,13 @@ FAKE = 1 << 20  # a 16-byte aligned non-null value; never dereferenced (rejected
     (lambda m: m.gemm_split_fp32(1, 64, 64, 64, FAKE, 66, 0, 1, FAKE, 64, 1, 1, 3, 0, FAKE, 64), -1),
     (lambda m: m.gemm_split_fp32(1, 64, 64, 64, FAKE, 64, 0, 1, FAKE, 64, 1, 1, 0, 0, FAKE, 64), -1),
     # attention: unsupported sizes, bad chains, small workspace, misaligned workspace
-    (lambda m: m.attention_split_fp32(2048, 32768, 64, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1 << 40), -3),
-    (lambda m: m.attention_split_fp32(2000, 32768, 128, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1 << 40), -3),
-    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 3, FAKE, FAKE, 1 << 40), -1),
-    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1024), -1),
-    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, FAKE, FAKE + 16, 1 << 40), -1),
+    (lambda m: m.attention_split_fp32(2048, 32768, 64, FAKE, FAKE, FAKE, 2, 1, FAKE, FAKE, 1 << 40), -3),
+    (lambda m: m.attention_split_fp32(2000, 32768, 128, FAKE, FAKE, FAKE, 2, 0, FAKE, FAKE, 1 << 40), -3),
+    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 3, 1, FAKE, FAKE, 1 << 40), -1),
+    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 2, FAKE, FAKE, 1 << 40), -1),
+    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 0, FAKE, FAKE, 1024), -1),
+    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 1, FAKE, FAKE, 1024), -1),
+    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 1, FAKE, FAKE + 16, 1 << 40), -1),
     # quantise / split: misaligned, negative n, bad dtype
     (lambda m: m.quantize_fp32(1, FAKE + 4, FAKE, 16), -1),
     (lambda m: m.quantize_fp32(1, FAKE, FAKE, -1), -1),
@@ -188,7 +190,12 @@ def test_empty_problems_are_noops_without_a_device(lib):
 
 
 def test_attention_workspace_size(lib):
-    b = lib.attention_workspace_bytes(2048, 32768, 128)
+    b = lib.attention_workspace_bytes(2048, 32768, 128, 0)
     assert b >= 2048 * 32768 * 4 + 2 * 2048 * 4 + 2048 * 128 * 4
+    f = lib.attention_workspace_bytes(2048, 32768, 128, 1)
+    # fp16 K and V^T plus per-slice partial O, m, l: far below the materialised scores
+    assert 2 * 32768 * 128 * 2 < f < b // 4
     with pytest.raises(lib.MflError):
-        lib.attention_workspace_bytes(2048, 32768, 96)
+        lib.attention_workspace_bytes(2048, 32768, 96, 1)
+    with pytest.raises(lib.MflError):
+        lib.attention_workspace_bytes(2048, 32768, 128, 5)

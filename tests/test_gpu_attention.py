@@ -1,6 +1,7 @@
 """attention_split_fp32 against the oracle: fp64 softmax(Q Q16(K)^T) Q16(V)
-with Q at its original values; normwise error <= 5e-6.  Small sizes in full,
-the 2048 x 32768 x 128 workload on sampled query rows."""
+with Q at its original values; normwise error <= 5e-6.  Both device
+algorithms (materialised scores, fused online softmax) and both chain counts;
+small sizes in full, the 2048 x 32768 x 128 workload on sampled query rows."""
 import numpy as np
 import pytest
 import torch
@@ -12,35 +13,49 @@ from oracle import reference as R
 from _gpu import dev32, device, host, say, stream
 
 pytestmark = pytest.mark.gpu
+ALGOS = [mfl.ATTN_MATERIALISED, mfl.ATTN_FUSED]
 
 
-def run_attention(q, k, v, chains):
+def run_attention(q, k, v, chains, algo):
     nq, d = q.shape
     nk = k.shape[0]
-    ws_bytes = mfl.attention_workspace_bytes(nq, nk, d)
+    ws_bytes = mfl.attention_workspace_bytes(nq, nk, d, algo)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device())
     o = torch.full((nq, d), np.nan, device=device())
-    mfl.attention_split_fp32(nq, nk, d, dev32(q), dev32(k), dev32(v), chains, o, ws, ws_bytes, stream())
+    mfl.attention_split_fp32(nq, nk, d, dev32(q), dev32(k), dev32(v), chains, algo, o, ws, ws_bytes, stream())
     return host(o)
 
 
+@pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("chains", [1, 2])
-@pytest.mark.parametrize("nq,nk", [(128, 128), (256, 1024), (384, 4096)])
-def test_attention_small(nq, nk, chains):
+@pytest.mark.parametrize("nq,nk", [(128, 128), (256, 1024), (384, 4096), (128, 8192)])
+def test_attention_small(nq, nk, chains, algo):
     q, k, v = inputs.attention(nq, nk)
-    say("attention", nq, nk, chains)
-    o = run_attention(q, k, v, chains)
+    say("attention", nq, nk, chains, algo)
+    o = run_attention(q, k, v, chains, algo)
     err = R.rel_error(o, R.attention_ref(q, k, v))
-    print(f"attention {nq}x{nk} chains={chains} err={err:.3e}")
+    print(f"attention {nq}x{nk} chains={chains} algo={algo} err={err:.3e}")
     assert err <= 5e-6
 
 
-def test_attention_uniform_closed_form():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_attention_uniform_closed_form(algo):
     """Q = 0: every score is 0, P is uniform and O is the column mean of Q16(V)."""
     _, k, v = inputs.attention(128, 2048)
     q = np.zeros((128, 128), np.float32)
-    say("attention Q=0")
-    o = run_attention(q, k, v, 2)
+    say("attention Q=0", algo)
+    o = run_attention(q, k, v, 2, algo)
+    assert R.rel_error(o, R.attention_ref(q, k, v)) <= 5e-6
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_attention_large_scores(algo):
+    """Scores of order 10 (Q scaled by 100): the running max moves between key
+    chunks and slices, exercising the rescaling of the fused kernel."""
+    q, k, v = inputs.attention(256, 4096)
+    q = (q * 100.0).astype(np.float32)
+    say("attention large scores", algo)
+    o = run_attention(q, k, v, 2, algo)
     assert R.rel_error(o, R.attention_ref(q, k, v)) <= 5e-6
 
 
@@ -49,10 +64,12 @@ def test_attention_full_size_sampled():
     errs = {}
     rows = np.random.default_rng(15).choice(2048, 64, replace=False)
     ref = R.attention_ref(q[rows], k, v)
-    for chains in (1, 2):
-        say("attention 2048x32768", chains)
-        o = run_attention(q, k, v, chains)
-        assert not np.isnan(o).any()
-        errs[chains] = R.rel_error(o[rows], ref)
-    print("attention full-size errors", errs)
-    assert errs[2] <= 5e-6
+    for algo in ALGOS:
+        for chains in (1, 2):
+            say("attention 2048x32768", chains, algo)
+            o = run_attention(q, k, v, chains, algo)
+            assert not np.isnan(o).any()
+            errs[(algo, chains)] = R.rel_error(o[rows], ref)
+    print("attention full-size errors (algo, chains):", errs)
+    assert errs[(mfl.ATTN_MATERIALISED, 2)] <= 5e-6
+    assert errs[(mfl.ATTN_FUSED, 2)] <= 5e-6
