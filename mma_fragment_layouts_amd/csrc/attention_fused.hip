@@ -4,93 +4,118 @@
 #include "attention_fused.hpp"
 
 namespace mfl {
-namespace {
+namespace attn_detail {
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// K (nk x 128 fp32) -> K16 (nk x 128 fp16, round to nearest even); 8 values per thread.
-__global__ __launch_bounds__(256) void attn_prep_k(const float* __restrict__ K, uint16_t* __restrict__ Kq,
-                                                   int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = *reinterpret_cast<const f32x4*>(K + i * 8);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(K + i * 8 + 4);
-  u32x4 o;
-  o[0] = pack2(to16<MFL_F16>(a[0]), to16<MFL_F16>(a[1]));
-  o[1] = pack2(to16<MFL_F16>(a[2]), to16<MFL_F16>(a[3]));
-  o[2] = pack2(to16<MFL_F16>(b[0]), to16<MFL_F16>(b[1]));
-  o[3] = pack2(to16<MFL_F16>(b[2]), to16<MFL_F16>(b[3]));
-  *reinterpret_cast<u32x4*>(Kq + i * 8) = o;
-}
-
-// V (nk x 128 fp32) -> V16^T (128 x nk fp16), keys of each 32-key block stored at
-// vt_key_pos(r).  One workgroup per 32-key block, transposed through LDS.
-__global__ __launch_bounds__(256) void attn_prep_vt(const float* __restrict__ V, uint16_t* __restrict__ Vt, int nk) {
-  __shared__ __attribute__((aligned(16))) uint16_t t[kAttnD * 32];
-  const int blk = blockIdx.x, tid = threadIdx.x;
-  {
-    const int key = tid >> 3, d0 = (tid & 7) * 16;
-    const float* src = V + ((int64_t)blk * 32 + key) * kAttnD + d0;
-    const int pos = vt_key_pos(key);
+// One workgroup per 32-key block (256 threads):
+//   K (nk x 128 fp32) -> K16 (nk x 128 fp16, round to nearest even);
+//   V (nk x 128 fp32) -> V16^T (128 x nk fp16), the keys of each 32-key block
+//   stored at vt_key_pos(r).  Thread (dim, half) gathers the 16 keys of
+//   storage positions 16 half .. 16 half + 15 for one dim: a wave's 64 lanes
+//   read 64 consecutive dims of one key per load.
+__global__ __launch_bounds__(256) void attn_prep(const float* __restrict__ K, const float* __restrict__ V,
+                                                 uint16_t* __restrict__ Kq, uint16_t* __restrict__ Vt, int nk) {
+  const int blk = blockIdx.x, t = threadIdx.x;
+  const int64_t base = (int64_t)blk * 32 * kAttnD;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) t[(d0 + 4 * q + e) * 32 + pos] = to16<MFL_F16>(v[e]);
-    }
+  for (int r = 0; r < 4; ++r) {
+    const int idx = (r * 256 + t) * 4;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(K + base + idx);
+    uint32_t w[2];
+    w[0] = pack2(to16<MFL_F16>(x[0]), to16<MFL_F16>(x[1]));
+    w[1] = pack2(to16<MFL_F16>(x[2]), to16<MFL_F16>(x[3]));
+    __builtin_memcpy(Kq + base + idx, w, 8);
   }
-  __syncthreads();
-  const int dim = tid >> 1, half = tid & 1;
-  uint16_t* dst = Vt + (int64_t)dim * nk + (int64_t)blk * 32 + half * 16;
-  *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(t + dim * 32 + half * 16);
-  *reinterpret_cast<u32x4*>(dst + 8) = *reinterpret_cast<const u32x4*>(t + dim * 32 + half * 16 + 8);
+  const int dim = t & (kAttnD - 1), half = t >> 7;
+  uint16_t h[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) h[p] = to16<MFL_F16>(V[base + (int64_t)vt_pos_key(16 * half + p) * kAttnD + dim]);
+  u32x4 o0, o1;
+  __builtin_memcpy(&o0, h, 16);
+  __builtin_memcpy(&o1, h + 8, 16);
+  uint16_t* dst = Vt + (int64_t)dim * nk + (int64_t)blk * 32 + 16 * half;
+  *reinterpret_cast<u32x4*>(dst) = o0;
+  *reinterpret_cast<u32x4*>(dst + 8) = o1;
 }
 
-// Grid: x = query blocks of 128, y = key slices of keys_per_split keys.
+// Packed hi/lo split of two fp32 values into fp16 pairs: hi = RNE16(x),
+// lo = RNE16(x - hi), with x - hi exact in fp32.
+struct Split2 {
+  uint32_t hi, lo;
+};
+__device__ __forceinline__ Split2 split2(float a, float b) {
+  const h16x2 h = __builtin_convertvector(f32x2{a, b}, h16x2);
+  const f32x2 hf = __builtin_convertvector(h, f32x2);
+  const h16x2 l = __builtin_convertvector(f32x2{a - hf.x, b - hf.y}, h16x2);
+  return {__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};
+}
+
+// Workgroup -> (query block, key slice).  With xcd_map the workgroups that an
+// XCD receives (hardware dispatch sends workgroup b to XCD b mod 8) cover a
+// contiguous range of key slices for every query block, so each XCD's L2 holds
+// only its own slices of K16 / V16^T.
+__device__ __forceinline__ void attn_block_of(int b, int nwg, int qblocks, int xcd_map, int& qb, int& sp) {
+  const int i = xcd_map ? (b & 7) * (nwg >> 3) + (b >> 3) : b;
+  qb = i % qblocks;
+  sp = i / qblocks;
+}
+
+// One workgroup: 128 queries (8 waves of 16) x one slice of keys_per_split keys.
+// Scores are kept in base-2 units (Q is scaled by log2 e before its split), so
+// P~ = 2^(s - mref).  mref is a per-query reference that only moves when a
+// chunk's maximum exceeds it by more than kAttnSlack; P~ then stays in
+// (0, 2^kAttnSlack] and the rescaling of O and l (by 2^(mref_old - mref_new))
+// is skipped for most chunks.  Any reference gives the same O = sum P~ V / sum P~
+// in real arithmetic.
+//
 template <int CHAINS, int STAGES>
-__global__ __launch_bounds__(256) void attn_fused_kernel(const float* __restrict__ Q, const uint16_t* __restrict__ Kq,
+__global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict__ Q, const uint16_t* __restrict__ Kq,
                                                          const uint16_t* __restrict__ Vt, float* __restrict__ Opart,
                                                          float* __restrict__ Mpart, float* __restrict__ Lpart, int nq,
-                                                         int nk, int keys_per_split) {
-  constexpr int BK = 64;                                  // LDS tile depth (dims for K16, keys for V16^T)
-  constexpr int KT = kAttnKV * BK;                        // one K16 half tile: 64 keys x 64 dims
-  constexpr int STAGE = 2 * KT + kAttnD * kAttnKV;        // K16 halves + V16^T tile (elements)
-  constexpr int LOADS = 8;                                // 1 KiB wave loads per stage per wave (32 / 4)
+                                                         int nk, int keys_per_split, int qblocks, int xcd_map) {
+  static_assert(kAttnQ == 128 && kAttnKV == 64 && kAttnD == 128, "tiling below assumes 128 x 64 x 128");
+  static_assert(STAGES >= 2, "at least double buffering");
+  constexpr int BK = 64;                    // LDS tile depth (dims for K16, keys for V16^T)
+  constexpr int KT = kAttnKV * BK;          // one K16 half tile: 64 keys x 64 dims
+  constexpr int STAGE = 2 * KT + kAttnD * kAttnKV;  // K16 halves + V16^T tile (elements)
+  constexpr int NW = 8;                     // waves per workgroup, 16 queries each
+  constexpr int LOADS = 32 / NW;            // 1 KiB wave loads per stage per wave
   __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE];
 
-  const int sp = blockIdx.y;
+  int qb, sp;
+  attn_block_of(blockIdx.x, gridDim.x, qblocks, xcd_map, qb, sp);
   const int kbeg = sp * keys_per_split;
   const int nchunks = keys_per_split / kAttnKV;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, g = lane >> 4;
-  const int qw = blockIdx.x * kAttnQ + wave * 32;
+  const int qw = qb * kAttnQ + wave * 16;
 
-  // Q^T fragments (B operand of GEMM1), split once: lane supplies query
-  // qw + 16*qt + lr, dims 32*d + 8*g .. +7.
-  u32x4 qh[2][4], ql[2][4];
+  // Q^T fragments (B operand of GEMM1), scaled by log2 e and split once: lane
+  // supplies query qw + lr, dims 32*d + 8*g .. +7.
+  u32x4 qh[4], ql[4];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int d = 0; d < 4; ++d) {
+    const float* p = Q + (int64_t)(qw + lr) * kAttnD + 32 * d + 8 * g;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(p), x1 = *reinterpret_cast<const f32x4*>(p + 4);
+    constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const float* p = Q + (int64_t)(qw + 16 * qt + lr) * kAttnD + 32 * d + 8 * g;
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(p), x1 = *reinterpret_cast<const f32x4*>(p + 4);
-      uint16_t h[8], l[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = e < 4 ? x0[e] : x1[e - 4];
-        h[e] = to16<MFL_F16>(x);
-        l[e] = to16<MFL_F16>(x - from16<MFL_F16>(h[e]));
-      }
-      __builtin_memcpy(&qh[qt][d], h, 16);
-      __builtin_memcpy(&ql[qt][d], l, 16);
+    for (int e = 0; e < 2; ++e) {
+      const Split2 s0 = split2(x0[2 * e] * kLog2e, x0[2 * e + 1] * kLog2e);
+      const Split2 s1 = split2(x1[2 * e] * kLog2e, x1[2 * e + 1] * kLog2e);
+      qh[d][e] = s0.hi;
+      ql[d][e] = s0.lo;
+      qh[d][2 + e] = s1.hi;
+      ql[d][2 + e] = s1.lo;
     }
+  }
 
   // Stage fill: 32 wave loads of 1 KiB (8 rows of 128 bytes); this wave issues
-  // blocks b = wave + 4*i.  Blocks 0-15: K16 half b/8, key rows 8*(b%8)..;
+  // blocks b = wave + NW*i.  Blocks 0-15: K16 half b/8, key rows 8*(b%8)..;
   // blocks 16-31: V16^T dim rows 8*(b-16)...  Physical chunk lane%8 of row
   // 8*blk + lane/8 receives logical chunk (lane%8) ^ swz(row).
   const rsrc_t rk = make_rsrc(Kq, (uint32_t)((int64_t)nk * kAttnD * 2));
@@ -98,7 +123,7 @@ __global__ __launch_bounds__(256) void attn_fused_kernel(const float* __restrict
   uint32_t voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int b = wave + 4 * i;  // wave-uniform
+    const int b = wave + NW * i;  // wave-uniform
     const int blk = b < 16 ? (b & 7) : b - 16;
     const int row = 8 * blk + (lane >> 3);
     const int lch = (lane & 7) ^ swz<BK>(row);
@@ -107,172 +132,198 @@ __global__ __launch_bounds__(256) void attn_fused_kernel(const float* __restrict
     else
       voff[i] = (uint32_t)(row * nk + lch * 8) * 2u;
   }
-  auto issue = [&](int stage, int key0) {
-    uint16_t* base = lds + stage * STAGE;
+  // With 8 waves, wave loads 0-1 (b = wave, wave + 8) fill K16 and 2-3 fill V16^T.
+  static_assert(NW == 8 && LOADS == 4, "K16 / V16^T split of the wave loads assumes 8 waves");
+  auto issue = [&](int chunk) {
+    uint16_t* base = lds + (chunk % STAGES) * STAGE;
+    const uint32_t key0 = (uint32_t)(kbeg + chunk * kAttnKV);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int b = wave + 4 * i;
-      if (b < 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(base + (b >> 3) * KT + (b & 7) * 8 * BK), 16,
-                                                 voff[i], (uint32_t)key0 * kAttnD * 2u, 0, 0);
+      const int b = wave + NW * i;
+      if (i < 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(base + i * KT + wave * 8 * BK), 16, voff[i],
+                                                 key0 * kAttnD * 2u, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(base + 2 * KT + (b - 16) * 8 * BK), 16, voff[i],
-                                                 (uint32_t)key0 * 2u, 0, 0);
+                                                 key0 * 2u, 0, 0);
     }
   };
 
   const FragOffsets<0, BK> fo(0, lane);  // lane row lr, chunk 4*kk + g
-  f32x4 oh[8][2], ol[8][2];
+
+  // GEMM1 of one chunk: S^T (64 keys x 16 queries) = K16 . (log2e Q)^T, hi and
+  // lo products in chains sh / sl (CHAINS == 2) or both in sh.
+  auto gemm1 = [&](int chunk, f32x4 (&sh)[4], f32x4 (&sl)[4]) {
+    const uint16_t* st = lds + (chunk % STAGES) * STAGE;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      oh[i][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      ol[i][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < 4; ++kt) {
+      sh[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sl[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
-
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nchunks) issue(s, kbeg + s * kAttnKV);
-  for (int c = 0; c < nchunks; ++c) {
-    if (c + STAGES - 2 < nchunks)
-      wait_vm<(STAGES - 2) * LOADS>();
-    else
-      wait_vm<0>();
-    __syncthreads();
-    if (c + STAGES - 1 < nchunks) issue((c + STAGES - 1) % STAGES, kbeg + (c + STAGES - 1) * kAttnKV);
-    const uint16_t* st = lds + (c % STAGES) * STAGE;
-
-    // GEMM1: S^T (keys x queries), 4 key tiles x 2 query tiles
-    f32x4 sh[4][2], sl[4][2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        sh[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sl[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       u32x4 a[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) a[kt] = lds_read16(st + (d >> 1) * KT, fo.off[d & 1] + kt * 16 * BK);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          sh[kt][qt] = mfma<0, MFL_F16>(a[kt], qh[qt][d], sh[kt][qt]);
-          if constexpr (CHAINS == 2)
-            sl[kt][qt] = mfma<0, MFL_F16>(a[kt], ql[qt][d], sl[kt][qt]);
-          else
-            sh[kt][qt] = mfma<0, MFL_F16>(a[kt], ql[qt][d], sh[kt][qt]);
-        }
-    }
-
-    // online softmax on the accumulators; lanes lr, lr+16, lr+32, lr+48 share a query
-    u32x4 ph[2][2], pl[2][2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      float cmax = -INFINITY;
-#pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        if constexpr (CHAINS == 2) sh[kt][qt] = sh[kt][qt] + sl[kt][qt];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, sh[kt][qt][j]);
+        sh[kt] = mfma<0, MFL_F16>(a[kt], qh[d], sh[kt]);
+        if constexpr (CHAINS == 2)
+          sl[kt] = mfma<0, MFL_F16>(a[kt], ql[d], sl[kt]);
+        else
+          sh[kt] = mfma<0, MFL_F16>(a[kt], ql[d], sh[kt]);
       }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-      const float mnew = fmaxf(m[qt], cmax);
-      const float sc = expf(m[qt] - mnew);
-      m[qt] = mnew;
-      lsum[qt] *= sc;
+    }
+  };
+
+  f32x4 oh[8], ol[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    oh[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ol[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float mref = -INFINITY, lsum = 0.f;
+
+  // Online softmax, in two parts.  Lanes lr, lr+16, lr+32, lr+48 share a query.
+  // (1) Chains added, chunk max, and the move of the reference when the max
+  // passes it by more than the slack (wave-uniform branch, rare after the
+  // first chunk).
+  auto update_ref = [&](f32x4 (&sh)[4], const f32x4 (&sl)[4]) {
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      if constexpr (CHAINS == 2) sh[kt] = sh[kt] + sl[kt];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, sh[kt][j]);
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    if (__builtin_amdgcn_ballot_w64(cmax > mref + kAttnSlack) != 0) {
+      const float mnew = fmaxf(mref, cmax);
+      const float sc = __builtin_amdgcn_exp2f(mref - mnew);  // 0 on the first chunk (mref = -inf)
+      mref = mnew;
+      lsum *= sc;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        oh[i][qt] = oh[i][qt] * sc;
-        if constexpr (CHAINS == 2) ol[i][qt] = ol[i][qt] * sc;
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        uint16_t h[8], l[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = expf(sh[2 * t + (e >> 2)][qt][e & 3] - mnew);
-          lsum[qt] += p;
-          h[e] = to16<MFL_F16>(p);
-          l[e] = to16<MFL_F16>(p - from16<MFL_F16>(h[e]));
-        }
-        __builtin_memcpy(&ph[t][qt], h, 16);
-        __builtin_memcpy(&pl[t][qt], l, 16);
+        oh[i] = oh[i] * sc;
+        if constexpr (CHAINS == 2) ol[i] = ol[i] * sc;
       }
     }
+  };
+  // (2) P~ = 2^(s - mref), its row-sum contribution, and the split P~^T
+  // fragments of GEMM2.
+  auto exp_split = [&](const f32x4 (&s)[4], u32x4 (&ph)[2], u32x4 (&pl)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // K positions 2e, 2e+1 of block t: keys of tile 2t (e < 2) or 2t+1
+        const f32x4& x = s[2 * t + (e >> 1)];
+        const float p0 = __builtin_amdgcn_exp2f(x[2 * (e & 1)] - mref);
+        const float p1 = __builtin_amdgcn_exp2f(x[2 * (e & 1) + 1] - mref);
+        lsum += p0;
+        lsum += p1;
+        const Split2 sp2 = split2(p0, p1);
+        ph[t][e] = sp2.hi;
+        pl[t][e] = sp2.lo;
+      }
+  };
 
-    // GEMM2: O^T (dims x queries) += V16^T . P~^T
-    const uint16_t* sv = st + 2 * KT;
+  // GEMM2 of one chunk: O^T (128 dims x 16 queries) += V16^T . P~^T.
+  auto gemm2 = [&](int chunk, const u32x4 (&ph)[2], const u32x4 (&pl)[2]) {
+    const uint16_t* sv = lds + (chunk % STAGES) * STAGE + 2 * KT;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const u32x4 a = lds_read16(sv, fo.off[t] + i * 16 * BK);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          oh[i][qt] = mfma<0, MFL_F16>(a, ph[t][qt], oh[i][qt]);
-          if constexpr (CHAINS == 2)
-            ol[i][qt] = mfma<0, MFL_F16>(a, pl[t][qt], ol[i][qt]);
-          else
-            oh[i][qt] = mfma<0, MFL_F16>(a, pl[t][qt], oh[i][qt]);
-        }
+        oh[i] = mfma<0, MFL_F16>(a, ph[t], oh[i]);
+        if constexpr (CHAINS == 2)
+          ol[i] = mfma<0, MFL_F16>(a, pl[t], ol[i]);
+        else
+          oh[i] = mfma<0, MFL_F16>(a, pl[t], oh[i]);
       }
+  };
+
+  // chunk c is waited for, then the stage of chunk c-1 is refilled with chunk
+  // c+STAGES-1 (every wave has passed the barrier, so chunk c-1 is consumed)
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nchunks) issue(s);
+  for (int c = 0; c < nchunks; ++c) {
+    if (c + STAGES - 2 < nchunks)
+      wait_vm<(STAGES - 2) * LOADS>();
+    else
+      wait_vm<0>();
+    __syncthreads();
+    if (c + STAGES - 1 < nchunks) issue(c + STAGES - 1);
+    f32x4 sh[4], sl[4];
+    gemm1(c, sh, sl);
+    u32x4 ph[2], pl[2];
+    update_ref(sh, sl);
+    exp_split(sh, ph, pl);
+    gemm2(c, ph, pl);
   }
 
-  // slice results: unnormalised O (chains added in fp32), m, and l summed over
-  // the four lanes of each query
+  // slice results: unnormalised O (chains added in fp32), mref and l summed
+  // over the four lanes of each query
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const int q = qw + lr;
+  float* orow = Opart + ((int64_t)sp * nq + q) * kAttnD;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    float lt = lsum[qt];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    const int q = qw + 16 * qt + lr;
-    float* orow = Opart + ((int64_t)sp * nq + q) * kAttnD;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      f32x4 o = oh[i][qt];
-      if constexpr (CHAINS == 2) o = o + ol[i][qt];
-      *reinterpret_cast<f32x4*>(orow + 16 * i + 4 * g) = o;
-    }
-    if (g == 0) {
-      Mpart[(int64_t)sp * nq + q] = m[qt];
-      Lpart[(int64_t)sp * nq + q] = lt;
-    }
+  for (int i = 0; i < 8; ++i) {
+    f32x4 o = oh[i];
+    if constexpr (CHAINS == 2) o = o + ol[i];
+    *reinterpret_cast<f32x4*>(orow + 16 * i + 4 * g) = o;
+  }
+  if (g == 0) {
+    Mpart[(int64_t)sp * nq + q] = mref;
+    Lpart[(int64_t)sp * nq + q] = lsum;
   }
 }
 
-// O[q][d] = sum_s w_s O_s[q][d] / sum_s w_s l_s[q], w_s = exp(m_s - max_s m_s),
-// slices taken in order s = 0, 1, ...
+// O[q][d] = sum_s w_s O_s[q][d] / sum_s w_s l_s[q], w_s = 2^(m_s - max_s m_s)
+// (m_s in base-2 units), slices taken in order s = 0, 1, ...  One thread per
+// query and 4 consecutive dims; S (the slice count) is a template parameter so
+// that all of a thread's loads are issued together.
+template <int S>
 __global__ __launch_bounds__(256) void attn_combine(const float* __restrict__ Opart, const float* __restrict__ Mpart,
-                                                    const float* __restrict__ Lpart, float* __restrict__ O, int nq,
-                                                    int splits) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)nq * kAttnD) return;
-  const int q = (int)(i / kAttnD);
-  float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, Mpart[(int64_t)s * nq + q]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float w = expf(Mpart[(int64_t)s * nq + q] - mx);
-    num += w * Opart[(int64_t)s * nq * kAttnD + i];
-    den += w * Lpart[(int64_t)s * nq + q];
+                                                    const float* __restrict__ Lpart, float* __restrict__ O, int nq) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // f32x4 index
+  if (i >= (int64_t)nq * (kAttnD / 4)) return;
+  const int q = (int)(i / (kAttnD / 4));
+  float m[S], l[S];
+  f32x4 o[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    m[s] = Mpart[(int64_t)s * nq + q];
+    l[s] = Lpart[(int64_t)s * nq + q];
+    o[s] = reinterpret_cast<const f32x4*>(Opart + (int64_t)s * nq * kAttnD)[i];
   }
-  O[i] = num / den;
+  float mx = m[0];
+#pragma unroll
+  for (int s = 1; s < S; ++s) mx = fmaxf(mx, m[s]);
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const float w = __builtin_amdgcn_exp2f(m[s] - mx);
+    num += w * o[s];
+    den += w * l[s];
+  }
+  reinterpret_cast<f32x4*>(O)[i] = num / den;
 }
 
-}  // namespace
+}  // namespace attn_detail
+
+using namespace attn_detail;
 
 // Sizes of the fused path's workspace pieces (bytes, each 256-aligned).
 int64_t attn_fused_splits(int64_t nq, int64_t nk) {
   const int64_t qblocks = nq / kAttnQ;
   int64_t s = 1;
-  while (s < 32 && qblocks * s < 512 && nk % (2 * s * kAttnKV) == 0) s *= 2;
+  while (s < 32 && qblocks * s < 256 && nk % (2 * s * kAttnKV) == 0) s *= 2;
   return s;
 }
 
@@ -296,18 +347,31 @@ int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, co
   float* mp = (float*)w;
   w += al(splits * nq * 4);
   float* lp = (float*)w;
-  const int64_t n8 = nk * kAttnD / 8;
-  hipLaunchKernelGGL(attn_prep_k, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, k, kq, n8);
-  hipLaunchKernelGGL(attn_prep_vt, dim3((unsigned)(nk / 32)), dim3(256), 0, st, v, vt, (int)nk);
-  const dim3 grid((unsigned)(nq / kAttnQ), (unsigned)splits);
+  hipLaunchKernelGGL(attn_prep, dim3((unsigned)(nk / 32)), dim3(256), 0, st, k, v, kq, vt, (int)nk);
+  const int qblocks = (int)(nq / kAttnQ);
+  const int nwg = qblocks * (int)splits;
+  const int xcd_map = nwg % 8 == 0;
   const int kps = (int)(nk / splits);
+  const dim3 grid((unsigned)nwg), block(512);
+  // two LDS stages: measured as fast as three, and a third adds nothing at
+  // one workgroup per CU
   if (chains == 2)
-    hipLaunchKernelGGL((attn_fused_kernel<2, 3>), grid, dim3(256), 0, st, q, kq, vt, op, mp, lp, (int)nq, (int)nk, kps);
+    hipLaunchKernelGGL((attn_fused_kernel<2, 2>), grid, block, 0, st, q, kq, vt, op, mp, lp, (int)nq, (int)nk, kps,
+                       qblocks, xcd_map);
   else
-    hipLaunchKernelGGL((attn_fused_kernel<1, 3>), grid, dim3(256), 0, st, q, kq, vt, op, mp, lp, (int)nq, (int)nk, kps);
-  const int64_t total = nq * kAttnD;
-  hipLaunchKernelGGL(attn_combine, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, op, mp, lp, o, (int)nq,
-                     (int)splits);
+    hipLaunchKernelGGL((attn_fused_kernel<1, 2>), grid, block, 0, st, q, kq, vt, op, mp, lp, (int)nq, (int)nk, kps,
+                       qblocks, xcd_map);
+  const int64_t vec = nq * kAttnD / 4;
+  const dim3 cgrid((unsigned)((vec + 255) / 256)), cblock(256);
+  switch (splits) {
+    case 1: hipLaunchKernelGGL(attn_combine<1>, cgrid, cblock, 0, st, op, mp, lp, o, (int)nq); break;
+    case 2: hipLaunchKernelGGL(attn_combine<2>, cgrid, cblock, 0, st, op, mp, lp, o, (int)nq); break;
+    case 4: hipLaunchKernelGGL(attn_combine<4>, cgrid, cblock, 0, st, op, mp, lp, o, (int)nq); break;
+    case 8: hipLaunchKernelGGL(attn_combine<8>, cgrid, cblock, 0, st, op, mp, lp, o, (int)nq); break;
+    case 16: hipLaunchKernelGGL(attn_combine<16>, cgrid, cblock, 0, st, op, mp, lp, o, (int)nq); break;
+    case 32: hipLaunchKernelGGL(attn_combine<32>, cgrid, cblock, 0, st, op, mp, lp, o, (int)nq); break;
+    default: return MFL_EUNSUPPORTED;  // the split chooser only returns powers of two up to 32
+  }
   return launch_status();
 }
 

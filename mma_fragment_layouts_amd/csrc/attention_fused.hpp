@@ -3,20 +3,21 @@
 // FP16 hi and lo half; "The fix": the halves accumulate in separate chains that
 // are added in plain fp32), with the scores never leaving the compute unit.
 //
-// Work split: a workgroup owns 128 queries (4 waves x 32) and one slice of the
+// Work split: a workgroup owns 128 queries (8 waves x 16) and one slice of the
 // keys.  Per 64-key chunk:
-//   GEMM1  S^T (64 keys x 32 queries per wave) = K16 . Q^T, with Q's hi and lo
+//   GEMM1  S^T (64 keys x 16 queries per wave) = K16 . Q^T, with Q's hi and lo
 //          halves as B fragments held in registers for the whole kernel (two
 //          chains, summed in fp32);
-//   online softmax on the accumulators: running max m per query (reduced across
-//          the four lanes that share a query), P~ = exp(S - m) in (0, 1], the
-//          output accumulators and the per-lane partial sum l rescaled by
-//          exp(m_old - m_new) when the max grows;
-//   GEMM2  O^T (128 dims x 32 queries) += V16^T . P~^T, with P~ split into fp16
+//   online softmax on the accumulators: per-query reference max (reduced
+//          across the four lanes that share a query), P~ = exp(S - mref), the
+//          output accumulators and the per-lane partial sum l rescaled when the
+//          reference moves;
+//   GEMM2  O^T (128 dims x 16 queries) += V16^T . P~^T, with P~ split into fp16
 //          hi/lo B fragments built directly from the S^T accumulator registers
 //          (two chains).
-// Each slice writes its unnormalised O, m and l; a combine kernel merges the
+// Each slice writes its unnormalised O, mref and l; a combine kernel merges the
 // slices with exp(m_s - max_s m_s) weights in a fixed order and divides by l.
+// The exponentials are taken base 2 on scores pre-scaled by log2 e.
 //
 // Layout trick: the S^T accumulator gives lane l (query l mod 16, group
 // g = l div 16) the keys 16*t' + 4g + j of each 16-key tile t'.  For GEMM2 the
@@ -33,6 +34,12 @@ namespace mfl {
 constexpr int kAttnQ = 128;   // queries per workgroup
 constexpr int kAttnKV = 64;   // keys per chunk
 constexpr int kAttnD = 128;   // head dimension
+// The reference max of a query moves only when a chunk's max (base-2 units)
+// exceeds it by more than this, so P~ <= 2^kAttnSlack (well inside fp16).
+constexpr float kAttnSlack = 8.f;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 
 // Storage position of key r (0..31) inside its 32-key block of V^T.
 MFL_HD constexpr int vt_key_pos(int r) { return 8 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3); }
@@ -45,5 +52,15 @@ constexpr bool vt_perm_is_bijection() {
   return true;
 }
 static_assert(vt_perm_is_bijection(), "V^T key permutation must be a bijection");
+
+// Key stored at position p (0..31) of a 32-key block: the inverse of vt_key_pos.
+MFL_HD constexpr int vt_pos_key(int p) { return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3); }
+
+constexpr bool vt_pos_key_is_inverse() {
+  for (int r = 0; r < 32; ++r)
+    if (vt_pos_key(vt_key_pos(r)) != r) return false;
+  return true;
+}
+static_assert(vt_pos_key_is_inverse(), "vt_pos_key must invert vt_key_pos");
 
 }  // namespace mfl

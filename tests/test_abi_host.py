@@ -28,6 +28,14 @@ def test_header_declares_and_library_exports_every_entry_point(lib):
     assert sorted(lib.EXPORTS) == declared
 
 
+def test_library_resolves_every_symbol():
+    """Binding every symbol at load time catches a kernel whose launch stub was
+    never emitted (lazy binding would only fail at the first call)."""
+    import ctypes
+    from mma_fragment_layouts_amd import _binding
+    ctypes.CDLL(_binding.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
 def test_version_and_status_strings(lib):
     assert lib.mfl_version() >= 100
     assert lib.status_string(0) == "MFL_OK"

@@ -28,7 +28,9 @@ def run_attention(q, k, v, chains, algo):
 
 @pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("chains", [1, 2])
-@pytest.mark.parametrize("nq,nk", [(128, 128), (256, 1024), (384, 4096), (128, 8192)])
+# key chunks of 64 per workgroup slice: 1, 3, 5, 1, 2 and 4 (odd counts take the
+# fused kernel's odd tail); (384, 4096) maps workgroups to XCDs by slice
+@pytest.mark.parametrize("nq,nk", [(128, 128), (128, 384), (256, 640), (256, 1024), (384, 4096), (128, 8192)])
 def test_attention_small(nq, nk, chains, algo):
     q, k, v = inputs.attention(nq, nk)
     say("attention", nq, nk, chains, algo)
