@@ -96,7 +96,10 @@ def cpu_baseline(a, bt):
             "seconds": round(dt, 3)}
 
 
-def extra_workloads(torch, mfl, inputs, stream):
+EXTRA = ("gemm_256", "block_repeat", "split", "attention")
+
+
+def extra_workloads(torch, mfl, inputs, stream, which=EXTRA):
     dev = torch.device("cuda:0")
     out = {}
 
@@ -106,7 +109,19 @@ def extra_workloads(torch, mfl, inputs, stream):
         mfl.quantize_fp32(dt, src, o, src.numel(), stream)
         return o
 
-    # single 256^3 fp16 GEMM (latency)
+    if "gemm_256" in which:
+        gemm_256(torch, mfl, inputs, stream, dev, q16, out)
+    if "block_repeat" in which:
+        block_repeat(torch, mfl, inputs, stream, dev, q16, out)
+    if "split" in which:
+        split(torch, mfl, inputs, stream, dev, out)
+    if "attention" in which:
+        attention(torch, mfl, inputs, stream, dev, out)
+    return out
+
+
+def gemm_256(torch, mfl, inputs, stream, dev, q16, out):
+    """Single 256^3 fp16 GEMM (latency)."""
     a, bt = inputs.gemm_small()
     da, db = q16(a, mfl.F16), q16(bt, mfl.F16)
     c = torch.empty((256, 256), device=dev)
@@ -115,7 +130,10 @@ def extra_workloads(torch, mfl, inputs, stream):
                            "bound": "latency (16 workgroups)",
                            "frac_mfma_peak": round(2 * 256 ** 3 / ms / 1e9 / PEAK_BF16_TFLOPS, 5)}
 
-    # block repeat, 2048^2 output, 64 repeats
+
+
+def block_repeat(torch, mfl, inputs, stream, dev, q16, out):
+    """2048^2 output, 64 repeats."""
     rep = {}
     for tm, tn, tk, th in [(64, 64, 64, 64), (64, 64, 64, 128), (64, 64, 64, 256), (32, 32, 32, 128),
                            (128, 128, 32, 128), (128, 128, 32, 256)]:
@@ -128,7 +146,9 @@ def extra_workloads(torch, mfl, inputs, stream):
             rep[f"{tm}x{tn}x{tk}/{th}/{name}"] = {"tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
     out["block_repeat"] = rep
 
-    # split fp32 GEMM 4096^3, bf16 pieces
+
+def split(torch, mfl, inputs, stream, dev, out):
+    """Split fp32 GEMM 4096^3, bf16 pieces."""
     a, bt = inputs.gemm_split()
     da = torch.from_numpy(a).to(dev)
     db = torch.from_numpy(bt).to(dev)
@@ -145,7 +165,9 @@ def extra_workloads(torch, mfl, inputs, stream):
     out["split_4096"] = sp
     del da, db, c
 
-    # attention pair 2048 x 32768 x 128
+
+def attention(torch, mfl, inputs, stream, dev, out):
+    """Attention pair 2048 x 32768 x 128, both algorithms, 1 and 2 chains."""
     q, k, v = inputs.attention()
     dq, dk, dv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
     o = torch.empty((2048, 128), device=dev)
@@ -161,7 +183,6 @@ def extra_workloads(torch, mfl, inputs, stream):
                                               "frac_mfma_peak": round(mf / PEAK_BF16_TFLOPS, 4)}
         del ws
     out["attention_2048x32768"] = att
-    return out
 
 
 def main():
@@ -171,6 +192,8 @@ def main():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--shape", type=int, default=0, help="MFMA shape of the GEMM fast path (0: 16x16x32, 1: 32x32x16)")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    p.add_argument("--extra", default=",".join(EXTRA),
+                   help="comma list of the other workloads to run (" + ", ".join(EXTRA) + ")")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run 3 plain device copies of 256 MiB (reference for the HBM byte counters)")
@@ -260,7 +283,12 @@ def main():
         del src, dst
     if not args.no_extra:
         log("other workloads")
-        result["workloads"] = extra_workloads(torch, mfl, inputs, stream)
+        which = tuple(w for w in args.extra.split(",") if w)
+        unknown = [w for w in which if w not in EXTRA]
+        if unknown:
+            print(f"unknown --extra workloads {unknown}; choose from {EXTRA}", file=sys.stderr)
+            sys.exit(2)
+        result["workloads"] = extra_workloads(torch, mfl, inputs, stream, which)
     if not args.no_cpu:
         log("cpu oracle baseline")
         result["cpu_baseline"] = cpu_baseline(a, bt)
