@@ -100,8 +100,62 @@ MFL_API int acc_matrix_offset(int shape, int lane, int j, int64_t row0, int64_t 
                       int64_t *out);
 
 /* ---------------------------------------------------------------------------
+ * Operand-fragment layout (host only, pure functions, no HIP calls).
+ *
+ * The other half of the layout contract: which lane supplies which element of
+ * the A (MN x K) and B (K x MN) operands of one MFMA.  cuda-oxide PR #474,
+ * section "Scope", leaves A/B fragments out of its accumulator API; the
+ * Tensor-core layout explainer (paragraph on fragments) says each thread
+ * holds specific pieces of A and B as well as of C.  These calls give them
+ * the same API shape and the same numeral treatment as the accumulator:
+ * lane l supplies the 8 consecutive K positions 8*(l div MN) + i (i = 0..7)
+ * of row l mod MN of A and of column l mod MN of B; MN = 16, K = 32 for
+ * MFL_MFMA_16X16X32 and MN = 32, K = 16 for MFL_MFMA_32X32X16, for f16 and
+ * bf16 alike.  Offsets are in the K-contiguous storage of the tile (A
+ * row-major m*K + k, B column-major n*K + k), the order the MFMA consumes.
+ * Unknown shape or operand, lane outside [0,64), i outside [0,8) or a NULL
+ * output pointer: MFL_EINVAL, nothing written.
+ * ------------------------------------------------------------------------- */
+
+typedef enum { MFL_OPERAND_A = 0, MFL_OPERAND_B = 1 } mfl_operand;
+
+/* Geometry of the operand tile: lanes (64), elements per lane (8), rows and
+ * cols of the operand as written (A: MN x K, B: K x MN). */
+MFL_API int mfl_operand_info(int shape, int operand, int *lanes, int *per_lane, int *rows, int *cols);
+
+/* Position of element i of `lane`: (m, k) for A, (k, n) for B. */
+MFL_API int operand_coords(int shape, int operand, int lane, int i, int *row, int *col);
+
+/* K-contiguous offset of (lane, i), computed in numeral form. */
+MFL_API int operand_offset(int shape, int operand, int lane, int i, int *offset);
+
+/* Inverse of operand_offset over [0, MN*K). */
+MFL_API int operand_decode(int shape, int operand, int offset, int *lane, int *i);
+
+/* Strided source of (lane, i) for an operand tile whose element origin is
+ * (row0, col0) (same row/col convention as operand_coords) in a matrix with
+ * leading dimension ld stored row-major (order MFL_ROW_MAJOR:
+ * (row0+row)*ld + col0+col) or column-major (MFL_COL_MAJOR:
+ * (col0+col)*ld + row0+row).  MFL_EOVERFLOW when the value does not fit int64
+ * or the contiguous coordinate reaches ld (the reading acc_matrix_offset
+ * uses); negative row0/col0, ld <= 0 or an unknown order: MFL_EINVAL. */
+MFL_API int operand_matrix_offset(int shape, int operand, int lane, int i, int64_t row0, int64_t col0,
+                                  int64_t ld, int order, int64_t *out);
+
+/* ---------------------------------------------------------------------------
  * Device entry points.
  * ------------------------------------------------------------------------- */
+
+/* Strided operand load (device): one wave gathers the fragment of `operand`
+ * for an operand tile at element origin (row0, col0) of a 16-bit matrix m
+ * (device memory, f16 or bf16 bits, leading dimension ld, order as in
+ * operand_matrix_offset) into frag[lane*8 + i] (512 16-bit values, device
+ * memory) — the load-side twin of acc_store_strided, and what mfma_probe
+ * takes as a_frag / b_frag.  MFL_EOVERFLOW if the tile's contiguous extent
+ * passes ld or its last element does not fit int64; MFL_EINVAL on NULL or
+ * odd pointers, negative origins, ld <= 0, unknown shape, operand or order. */
+MFL_API int operand_load_strided(int shape, int operand, const void *m, int64_t row0, int64_t col0,
+                                 int64_t ld, int order, void *frag, void *stream);
 
 /* Strided epilogue store (device): one wave scatters a lane-major accumulator
  * acc[lane*J + j] (64*J fp32, device memory) into C at element origin

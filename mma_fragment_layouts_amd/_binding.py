@@ -22,6 +22,7 @@ F16, BF16 = 0, 1
 ROW_MAJOR, COL_MAJOR = 0, 1
 ROUND, SPLIT = 0, 1
 ATTN_MATERIALISED, ATTN_FUSED = 0, 1
+OPERAND_A, OPERAND_B = 0, 1
 
 _i32, _i64, _vp = C.c_int, C.c_int64, C.c_void_p
 _pi32, _pi64 = C.POINTER(C.c_int), C.POINTER(C.c_int64)
@@ -34,6 +35,12 @@ _SIGNATURES = {
     "acc_offset": (_i32, [_i32, _i32, _i32, _pi32]),
     "acc_decode": (_i32, [_i32, _i32, _pi32, _pi32]),
     "acc_matrix_offset": (_i32, [_i32, _i32, _i32, _i64, _i64, _i64, _pi64]),
+    "mfl_operand_info": (_i32, [_i32, _i32, _pi32, _pi32, _pi32, _pi32]),
+    "operand_coords": (_i32, [_i32, _i32, _i32, _i32, _pi32, _pi32]),
+    "operand_offset": (_i32, [_i32, _i32, _i32, _i32, _pi32]),
+    "operand_decode": (_i32, [_i32, _i32, _i32, _pi32, _pi32]),
+    "operand_matrix_offset": (_i32, [_i32, _i32, _i32, _i32, _i64, _i64, _i64, _i32, _pi64]),
+    "operand_load_strided": (_i32, [_i32, _i32, _vp, _i64, _i64, _i64, _i32, _vp, _vp]),
     "acc_store_strided": (_i32, [_i32, _vp, _vp, _i64, _i64, _i64, _vp]),
     "mfma_probe": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "quantize_fp32": (_i32, [_i32, _vp, _vp, _i64, _vp]),
@@ -147,6 +154,46 @@ def acc_matrix_offset(shape: int, lane: int, j: int, row0: int, col0: int, ld: i
         return None
     _check(st, "acc_matrix_offset")
     return o.value
+
+
+def mfl_operand_info(shape: int, operand: int) -> Tuple[int, int, int, int]:
+    v = [C.c_int() for _ in range(4)]
+    _check(load().mfl_operand_info(shape, operand, *[C.byref(x) for x in v]), "mfl_operand_info")
+    return tuple(x.value for x in v)
+
+
+def operand_coords(shape: int, operand: int, lane: int, i: int) -> Tuple[int, int]:
+    r, c = C.c_int(), C.c_int()
+    _check(load().operand_coords(shape, operand, lane, i, C.byref(r), C.byref(c)), "operand_coords")
+    return r.value, c.value
+
+
+def operand_offset(shape: int, operand: int, lane: int, i: int) -> int:
+    o = C.c_int()
+    _check(load().operand_offset(shape, operand, lane, i, C.byref(o)), "operand_offset")
+    return o.value
+
+
+def operand_decode(shape: int, operand: int, offset: int) -> Tuple[int, int]:
+    lane, i = C.c_int(), C.c_int()
+    _check(load().operand_decode(shape, operand, offset, C.byref(lane), C.byref(i)), "operand_decode")
+    return lane.value, i.value
+
+
+def operand_matrix_offset(shape: int, operand: int, lane: int, i: int, row0: int, col0: int, ld: int,
+                          order: int) -> Optional[int]:
+    """Strided source, or None when the library reports MFL_EOVERFLOW."""
+    o = C.c_int64()
+    st = load().operand_matrix_offset(shape, operand, lane, i, row0, col0, ld, order, C.byref(o))
+    if st == EOVERFLOW:
+        return None
+    _check(st, "operand_matrix_offset")
+    return o.value
+
+
+def operand_load_strided(shape, operand, m, row0, col0, ld, order, frag, stream=None) -> None:
+    _check(load().operand_load_strided(shape, operand, _ptr(m), row0, col0, ld, order, _ptr(frag), _stream(stream)),
+           "operand_load_strided")
 
 
 def acc_store_strided(shape, acc, c, row0, col0, ldc, stream=None) -> None:

@@ -86,6 +86,9 @@ struct TileLoader {
 template <int SHAPE, int BK>
 struct FragOffsets {
   static constexpr int MN = Shape<SHAPE>::MN, KM = Shape<SHAPE>::K, CPK = KM / 8, KSTEPS = BK / KM;
+  // lane row lane % MN, chunk lane / MN: the exported operand numeral (layout.hpp)
+  static_assert(operand_layout(SHAPE).rows == MN && operand_layout(SHAPE).cols == KM,
+                "fragment reads must follow the operand numeral of the instruction");
   int off[KSTEPS];
   __device__ __forceinline__ FragOffsets(int row0, int lane) {
     const int lr = lane % MN, lk = lane / MN;

@@ -21,6 +21,14 @@
 // the same phenomenon the page points out for m16n8k16: j 0->1 is one row, j 3->4
 // is eight rows.
 //
+// The operand fragments of the same instructions (which lane supplies which A
+// and B element; the page leaves them out of scope, "Scope" section) are
+// numerals of the same kind over the K-contiguous storage of the operand tile
+// (A row-major m*K + k, B column-major n*K + k): lane l supplies the 8
+// consecutive K positions 8*(l div MN) + i of row (A) or column (B) l mod MN.
+//   16x16x32: offset = i*1 + (lane>>4)*8 + (lane&15)*32          span 512
+//   32x32x16: offset = i*1 + (lane>>5)*8 + (lane&31)*16          span 512
+//
 // Everything here is constexpr and usable from host and device code.
 #pragma once
 #include <stdint.h>
@@ -44,7 +52,7 @@ struct Digit {
 
 struct AccLayout {
   int lanes;      // lanes of the wave holding the tile
-  int per_lane;   // accumulator values per lane (J)
+  int per_lane;   // values per lane (J for accumulators, 8 for operands)
   int rows, cols; // tile shape; offsets are row-major: row*cols + col
   int ndigits;
   Digit d[4];     // lowest place first
@@ -55,6 +63,12 @@ constexpr AccLayout kAcc16x16x32 = {64, 4, 16, 16, 3, {{kLane, 0, 16}, {kJ, 0, 4
 constexpr AccLayout kAcc32x32x16 = {64, 16, 32, 32, 4, {{kLane, 0, 32}, {kJ, 0, 4}, {kLane, 5, 2}, {kJ, 2, 4}}};
 
 MFL_HD constexpr const AccLayout& acc_layout(int shape) { return shape == 0 ? kAcc16x16x32 : kAcc32x32x16; }
+
+// Operand numerals: rows = MN, cols = K of the K-contiguous storage (j = i).
+constexpr AccLayout kOp16x16x32 = {64, 8, 16, 32, 3, {{kJ, 0, 8}, {kLane, 4, 4}, {kLane, 0, 16}, {0, 0, 1}}};
+constexpr AccLayout kOp32x32x16 = {64, 8, 32, 16, 3, {{kJ, 0, 8}, {kLane, 5, 2}, {kLane, 0, 32}, {0, 0, 1}}};
+
+MFL_HD constexpr const AccLayout& operand_layout(int shape) { return shape == 0 ? kOp16x16x32 : kOp32x32x16; }
 
 MFL_HD constexpr int acc_span(const AccLayout& L) {
   int s = 1;
@@ -107,5 +121,21 @@ constexpr bool layout_self_consistent(const AccLayout& L) {
 }
 static_assert(layout_self_consistent(kAcc16x16x32), "16x16x32 numeral is not a bijection");
 static_assert(layout_self_consistent(kAcc32x32x16), "32x32x16 numeral is not a bijection");
+static_assert(layout_self_consistent(kOp16x16x32), "16x16x32 operand numeral is not a bijection");
+static_assert(layout_self_consistent(kOp32x32x16), "32x32x16 operand numeral is not a bijection");
+
+// The GEMM kernels read a lane's operand fragment as one 16-byte chunk: row
+// (or column) lane mod MN, K positions from 8*(lane div MN).  That is element
+// i = 0 of the operand numeral, and the 8 elements of a lane are consecutive.
+constexpr bool operand_chunks_match(const AccLayout& L) {
+  for (int lane = 0; lane < L.lanes; ++lane) {
+    if (acc_offset(L, lane, 0) != (lane % L.rows) * L.cols + 8 * (lane / L.rows)) return false;
+    for (int i = 1; i < L.per_lane; ++i)
+      if (acc_offset(L, lane, i) != acc_offset(L, lane, 0) + i) return false;
+  }
+  return true;
+}
+static_assert(operand_chunks_match(kOp16x16x32) && operand_chunks_match(kOp32x32x16),
+              "kernel fragment reads disagree with the operand numerals");
 
 }  // namespace mfl

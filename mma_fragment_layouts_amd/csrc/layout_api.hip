@@ -1,5 +1,6 @@
-// C ABI of the accumulator-fragment layout (host), the strided epilogue store
-// and the single-MFMA probe (device), status strings.
+// C ABI of the accumulator- and operand-fragment layouts (host), the strided
+// epilogue store, the strided operand load and the single-MFMA probe (device),
+// status strings.
 //
 // cuda-oxide PR #474, section "API": acc_coords, acc_offset, acc_matrix_offset
 // (None on overflow) and acc_decode, here for the CDNA4 accumulator layouts and
@@ -15,6 +16,38 @@ bool valid_shape(int shape) { return shape == MFL_MFMA_16X16X32 || shape == MFL_
 bool valid_point(int shape, int lane, int j) {
   const AccLayout& L = acc_layout(shape);
   return lane >= 0 && lane < L.lanes && j >= 0 && j < L.per_lane;
+}
+
+bool valid_operand(int operand) { return operand == MFL_OPERAND_A || operand == MFL_OPERAND_B; }
+
+bool valid_operand_point(int shape, int lane, int i) {
+  const AccLayout& L = operand_layout(shape);
+  return lane >= 0 && lane < L.lanes && i >= 0 && i < L.per_lane;
+}
+
+// (row, col) of operand element i of `lane` as the operand is written: (m, k)
+// for A, (k, n) for B, from the K-contiguous numeral offset mn*K + k.
+MFL_HD constexpr void operand_rc(const AccLayout& L, int operand, int lane, int i, int* row, int* col) {
+  const int off = mfl::acc_offset(L, lane, i);
+  const int mn = off / L.cols, k = off % L.cols;
+  *row = operand == MFL_OPERAND_A ? mn : k;
+  *col = operand == MFL_OPERAND_A ? k : mn;
+}
+
+// One wave: gather each lane's 8 operand elements from a strided matrix.
+template <int SHAPE>
+__global__ __launch_bounds__(64) void operand_load_kernel(const uint16_t* __restrict__ m, int64_t row0, int64_t col0,
+                                                         int64_t ld, int order, int operand,
+                                                         uint16_t* __restrict__ frag) {
+  constexpr AccLayout L = operand_layout(SHAPE);
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < L.per_lane; ++i) {
+    int r, c;
+    operand_rc(L, operand, lane, i, &r, &c);
+    const int64_t idx = order == MFL_ROW_MAJOR ? (row0 + r) * ld + col0 + c : (col0 + c) * ld + row0 + r;
+    frag[lane * L.per_lane + i] = m[idx];
+  }
 }
 
 // One wave: write lane-major accumulator values through the layout.
@@ -102,6 +135,82 @@ extern "C" int acc_matrix_offset(int shape, int lane, int j, int64_t row0, int64
   if (__builtin_add_overflow(rl, c, &o)) return MFL_EOVERFLOW;
   *out = o;
   return MFL_OK;
+}
+
+extern "C" int mfl_operand_info(int shape, int operand, int* lanes, int* per_lane, int* rows, int* cols) {
+  if (!valid_shape(shape) || !valid_operand(operand) || !lanes || !per_lane || !rows || !cols) return MFL_EINVAL;
+  const AccLayout& L = operand_layout(shape);  // rows = MN, cols = K
+  *lanes = L.lanes;
+  *per_lane = L.per_lane;
+  *rows = operand == MFL_OPERAND_A ? L.rows : L.cols;
+  *cols = operand == MFL_OPERAND_A ? L.cols : L.rows;
+  return MFL_OK;
+}
+
+extern "C" int operand_coords(int shape, int operand, int lane, int i, int* row, int* col) {
+  if (!valid_shape(shape) || !valid_operand(operand) || !row || !col || !valid_operand_point(shape, lane, i))
+    return MFL_EINVAL;
+  operand_rc(operand_layout(shape), operand, lane, i, row, col);
+  return MFL_OK;
+}
+
+extern "C" int operand_offset(int shape, int operand, int lane, int i, int* offset) {
+  if (!valid_shape(shape) || !valid_operand(operand) || !offset || !valid_operand_point(shape, lane, i))
+    return MFL_EINVAL;
+  *offset = mfl::acc_offset(operand_layout(shape), lane, i);
+  return MFL_OK;
+}
+
+extern "C" int operand_decode(int shape, int operand, int offset, int* lane, int* i) {
+  if (!valid_shape(shape) || !valid_operand(operand) || !lane || !i) return MFL_EINVAL;
+  const AccLayout& L = operand_layout(shape);
+  if (offset < 0 || offset >= L.rows * L.cols) return MFL_EINVAL;
+  mfl::acc_decode(L, offset, lane, i);
+  return MFL_OK;
+}
+
+extern "C" int operand_matrix_offset(int shape, int operand, int lane, int i, int64_t row0, int64_t col0, int64_t ld,
+                                     int order, int64_t* out) {
+  if (!valid_shape(shape) || !valid_operand(operand) || !out || !valid_operand_point(shape, lane, i)) return MFL_EINVAL;
+  if (row0 < 0 || col0 < 0 || ld <= 0 || (order != MFL_ROW_MAJOR && order != MFL_COL_MAJOR)) return MFL_EINVAL;
+  int r, c;
+  operand_rc(operand_layout(shape), operand, lane, i, &r, &c);
+  // outer / inner: the strided and the contiguous coordinate of the element
+  const int64_t o0 = order == MFL_ROW_MAJOR ? row0 : col0, i0 = order == MFL_ROW_MAJOR ? col0 : row0;
+  const int ro = order == MFL_ROW_MAJOR ? r : c, ri = order == MFL_ROW_MAJOR ? c : r;
+  int64_t outer, inner, t, o;
+  if (__builtin_add_overflow(i0, (int64_t)ri, &inner)) return MFL_EOVERFLOW;
+  if (inner >= ld) return MFL_EOVERFLOW;  // would spill into the next row / column
+  if (__builtin_add_overflow(o0, (int64_t)ro, &outer)) return MFL_EOVERFLOW;
+  if (__builtin_mul_overflow(outer, ld, &t)) return MFL_EOVERFLOW;
+  if (__builtin_add_overflow(t, inner, &o)) return MFL_EOVERFLOW;
+  *out = o;
+  return MFL_OK;
+}
+
+extern "C" int operand_load_strided(int shape, int operand, const void* m, int64_t row0, int64_t col0, int64_t ld,
+                                    int order, void* frag, void* stream) {
+  if (!valid_shape(shape) || !valid_operand(operand) || !m || !frag) return MFL_EINVAL;
+  if (row0 < 0 || col0 < 0 || ld <= 0 || (order != MFL_ROW_MAJOR && order != MFL_COL_MAJOR)) return MFL_EINVAL;
+  if (((uintptr_t)m & 1) || ((uintptr_t)frag & 1)) return MFL_EINVAL;
+  int lanes, per_lane, rows, cols;
+  mfl_operand_info(shape, operand, &lanes, &per_lane, &rows, &cols);
+  // The tile's last element must fit: contiguous extent within ld, offset in int64.
+  const int64_t o0 = order == MFL_ROW_MAJOR ? row0 : col0, i0 = order == MFL_ROW_MAJOR ? col0 : row0;
+  const int no = order == MFL_ROW_MAJOR ? rows : cols, ni = order == MFL_ROW_MAJOR ? cols : rows;
+  int64_t last, t;
+  if (i0 > ld - ni) return MFL_EOVERFLOW;
+  if (__builtin_add_overflow(o0, (int64_t)(no - 1), &last) || __builtin_mul_overflow(last, ld, &t) ||
+      __builtin_add_overflow(t, i0 + ni - 1, &t))
+    return MFL_EOVERFLOW;
+  hipStream_t s = (hipStream_t)stream;
+  if (shape == MFL_MFMA_16X16X32)
+    hipLaunchKernelGGL(operand_load_kernel<0>, dim3(1), dim3(64), 0, s, (const uint16_t*)m, row0, col0, ld, order,
+                       operand, (uint16_t*)frag);
+  else
+    hipLaunchKernelGGL(operand_load_kernel<1>, dim3(1), dim3(64), 0, s, (const uint16_t*)m, row0, col0, ld, order,
+                       operand, (uint16_t*)frag);
+  return launch_status();
 }
 
 extern "C" int acc_store_strided(int shape, const float* acc, float* c, int64_t row0, int64_t col0, int64_t ldc,

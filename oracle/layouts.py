@@ -17,6 +17,12 @@ loops over every point, for any map given in row/col form:
     whose registers name their own coordinates; they have no printed values in
     the pages (parity for them rests on the hardware probe).
 
+The same machinery covers the operand fragments of those two instructions
+(which lane supplies which element of A and B), the half of the layout contract
+the cuda-oxide page leaves out of scope ("Scope" section).  Operand maps are
+pinned like the accumulator maps: bijection here, hardware on the device (a raw
+MFMA fed through these maps must reproduce a host matmul exactly).
+
 The inverse map (decode) is built here by inverting the enumeration, never by a
 closed formula, so that it is independent of the library's numeral arithmetic.
 """
@@ -61,6 +67,90 @@ MFMA_32X32X16 = FragmentMap(
 )
 
 MAPS = {m.name: m for m in (M16N8K16, MFMA_16X16X32, MFMA_32X32X16)}
+
+
+# ---- operand fragments of the CDNA4 f16/bf16 MFMA instructions
+#
+# Each lane supplies 8 consecutive K positions of one row of A (MN x K) and of
+# one column of B (K x MN): lane l holds A[l mod MN][8*(l div MN) + i] and
+# B[8*(l div MN) + i][l mod MN], i = 0..7.  With 64 lanes, 16x16x32 has four
+# K groups of 8 (K = 32) and 32x32x16 has two (K = 16).  coords are (row, col)
+# of the operand as written: (m, k) for A, (k, n) for B.
+
+@dataclass(frozen=True)
+class OperandMap:
+    name: str
+    operand: str        # "A" or "B"
+    lanes: int
+    per_lane: int       # 16-bit elements per lane (8: one 16-byte register group)
+    rows: int           # A: MN, B: K
+    cols: int           # A: K,  B: MN
+    coords: Callable[[int, int], Tuple[int, int]]   # (lane, i) -> (row, col)
+
+
+def _operand_map(name: str, operand: str, mn: int, k: int) -> OperandMap:
+    if operand == "A":
+        return OperandMap(name, "A", 64, 8, mn, k, lambda lane, i: (lane % mn, 8 * (lane // mn) + i))
+    return OperandMap(name, "B", 64, 8, k, mn, lambda lane, i: (8 * (lane // mn) + i, lane % mn))
+
+
+OPERAND_MAPS = {
+    (0, "A"): _operand_map("mfma_16x16x32.A", "A", 16, 32),
+    (0, "B"): _operand_map("mfma_16x16x32.B", "B", 16, 32),
+    (1, "A"): _operand_map("mfma_32x32x16.A", "A", 32, 16),
+    (1, "B"): _operand_map("mfma_32x32x16.B", "B", 32, 16),
+}
+
+
+def operand_offset(om: OperandMap, lane: int, i: int) -> int:
+    """Offset of (lane, i) in the K-contiguous storage of the operand tile:
+    A row-major (m*K + k), B column-major (n*K + k)."""
+    r, c = om.coords(lane, i)
+    return r * om.cols + c if om.operand == "A" else c * om.rows + r
+
+
+def operand_decode_table(om: OperandMap) -> Dict[int, Tuple[int, int]]:
+    """Inverse of ``operand_offset`` by enumeration; raises on a shared offset."""
+    inv: Dict[int, Tuple[int, int]] = {}
+    for lane in range(om.lanes):
+        for i in range(om.per_lane):
+            o = operand_offset(om, lane, i)
+            if o in inv:
+                raise ValueError(f"{om.name}: offset {o} owned twice")
+            inv[o] = (lane, i)
+    return inv
+
+
+def operand_is_bijection(om: OperandMap) -> bool:
+    """Every (row, col) of the operand tile supplied by exactly one (lane, i)."""
+    if om.lanes * om.per_lane != om.rows * om.cols:
+        return False
+    own = [[0] * om.cols for _ in range(om.rows)]
+    for lane in range(om.lanes):
+        for i in range(om.per_lane):
+            r, c = om.coords(lane, i)
+            if not (0 <= r < om.rows and 0 <= c < om.cols):
+                return False
+            own[r][c] += 1
+    return all(v == 1 for row in own for v in row)
+
+
+def operand_matrix_offset(om: OperandMap, lane: int, i: int, row0: int, col0: int, ld: int,
+                          order: int) -> Optional[int]:
+    """Element offset of (lane, i) when the operand tile's origin sits at
+    (row0, col0) of a matrix with leading dimension ``ld``: row-major (order 0)
+    (row0+row)*ld + col0+col, column-major (order 1) (col0+col)*ld + row0+row.
+    None on overflow: the contiguous coordinate reaches ``ld`` (it would spill
+    into the next row or column) or the value does not fit a signed 64-bit
+    offset — the reading taken for the accumulator's strided destination."""
+    if row0 < 0 or col0 < 0 or ld <= 0 or order not in (0, 1):
+        raise ValueError("negative origin, non-positive leading dimension or bad order")
+    r, c = om.coords(lane, i)
+    outer, inner = (row0 + r, col0 + c) if order == 0 else (col0 + c, row0 + r)
+    if inner >= ld:
+        return None
+    out = outer * ld + inner
+    return None if out > INT64_MAX else out
 
 
 def ownership(fm: FragmentMap) -> List[List[int]]:

@@ -136,6 +136,110 @@ def test_layout_argument_errors(lib):
         lib.acc_matrix_offset(0, 0, 0, 0, 0, 0)
 
 
+OPS = {0: "A", 1: "B"}
+
+
+@pytest.mark.parametrize("operand", [0, 1])
+@pytest.mark.parametrize("shape", [0, 1])
+def test_operand_info(lib, shape, operand):
+    om = OL.OPERAND_MAPS[(shape, OPS[operand])]
+    assert lib.mfl_operand_info(shape, operand) == (om.lanes, om.per_lane, om.rows, om.cols)
+
+
+@pytest.mark.parametrize("operand", [0, 1])
+@pytest.mark.parametrize("shape", [0, 1])
+def test_operand_coords_offsets_decode_match_oracle_exhaustively(lib, shape, operand):
+    om = OL.OPERAND_MAPS[(shape, OPS[operand])]
+    inv = OL.operand_decode_table(om)
+    for lane in range(64):
+        for i in range(8):
+            assert lib.operand_coords(shape, operand, lane, i) == om.coords(lane, i)
+            assert lib.operand_offset(shape, operand, lane, i) == OL.operand_offset(om, lane, i)
+    for o in range(om.rows * om.cols):
+        assert lib.operand_decode(shape, operand, o) == inv[o]
+
+
+@pytest.mark.parametrize("operand", [0, 1])
+@pytest.mark.parametrize("shape", [0, 1])
+def test_six_operand_layout_properties(lib, shape, operand):
+    """The cuda-oxide page's six checks ("Tests" section), on the operand maps."""
+    om = OL.OPERAND_MAPS[(shape, OPS[operand])]
+    L, E, R, Cc = lib.mfl_operand_info(shape, operand)
+    kdim = Cc if operand == 0 else R
+    pts = [(l, i) for l in range(L) for i in range(E)]
+    # 1. bijection via an ownership map
+    own = [[0] * Cc for _ in range(R)]
+    for l, i in pts:
+        r, c = lib.operand_coords(shape, operand, l, i)
+        own[r][c] += 1
+    assert all(v == 1 for row in own for v in row)
+    # 2. numeral form agrees with the row/col form (K-contiguous storage)
+    for l, i in pts:
+        r, c = lib.operand_coords(shape, operand, l, i)
+        mn, k = (r, c) if operand == 0 else (c, r)
+        assert lib.operand_offset(shape, operand, l, i) == mn * kdim + k
+    # 3. decode is a true inverse on all points, both directions
+    for l, i in pts:
+        assert lib.operand_decode(shape, operand, lib.operand_offset(shape, operand, l, i)) == (l, i)
+    for o in range(R * Cc):
+        assert lib.operand_offset(shape, operand, *lib.operand_decode(shape, operand, o)) == o
+    # 4. the element index moves along K only; the lane's high digit moves K by 8
+    mnn = 64 * 8 // kdim
+    for l in range(L):
+        r0, c0 = lib.operand_coords(shape, operand, l, 0)
+        step = (0, 1) if operand == 0 else (1, 0)
+        assert lib.operand_coords(shape, operand, l, 1) == (r0 + step[0], c0 + step[1])
+        if l + mnn < L:
+            r1, c1 = lib.operand_coords(shape, operand, l + mnn, 0)
+            assert (r1 - r0, c1 - c0) == (8 * step[0], 8 * step[1])
+    # 5. disjointness under strided placement, both orders
+    for order in (0, 1):
+        ld = 3 * (Cc if order == 0 else R) + 8
+        seen = set()
+        for tr in range(3):
+            for tc in range(3):
+                for l, i in pts:
+                    o = lib.operand_matrix_offset(shape, operand, l, i, tr * R, tc * Cc, ld, order)
+                    assert o is not None and o not in seen
+                    assert o == OL.operand_matrix_offset(om, l, i, tr * R, tc * Cc, ld, order)
+                    seen.add(o)
+    # 6. overflow rejection
+    assert lib.operand_matrix_offset(shape, operand, L - 1, E - 1, 0, Cc, 2 * Cc - 1, 0) is None
+    assert lib.operand_matrix_offset(shape, operand, L - 1, E - 1, R, 0, 2 * R - 1, 1) is None
+    assert lib.operand_matrix_offset(shape, operand, L - 1, E - 1, 1 << 62, 0, 64, 0) is None
+
+
+def test_operand_matrix_offset_matches_oracle_on_random_origins(lib):
+    import random
+    rnd = random.Random(7)
+    for _ in range(2000):
+        shape, operand, order = rnd.randint(0, 1), rnd.randint(0, 1), rnd.randint(0, 1)
+        om = OL.OPERAND_MAPS[(shape, OPS[operand])]
+        lane, i = rnd.randrange(64), rnd.randrange(8)
+        inner = om.cols if order == 0 else om.rows
+        ld = rnd.choice([inner, inner + 1, 4096, 4160, (1 << 40) + 7])
+        o_outer = rnd.choice([0, 1, 17, 4095, (1 << 22), (1 << 62) // ld])
+        o_inner = rnd.choice([0, 1, ld - inner, max(0, ld - 1)])
+        row0, col0 = (o_outer, o_inner) if order == 0 else (o_inner, o_outer)
+        assert (lib.operand_matrix_offset(shape, operand, lane, i, row0, col0, ld, order)
+                == OL.operand_matrix_offset(om, lane, i, row0, col0, ld, order))
+
+
+def test_operand_argument_errors(lib):
+    for bad in [(2, 0, 0, 0), (0, 2, 0, 0), (0, -1, 0, 0), (0, 0, 64, 0), (1, 1, 0, 8), (1, 0, 0, -1)]:
+        with pytest.raises(lib.MflError) as e:
+            lib.operand_coords(*bad)
+        assert e.value.status == lib.EINVAL
+    with pytest.raises(lib.MflError):
+        lib.operand_decode(0, 0, 512)
+    with pytest.raises(lib.MflError):
+        lib.operand_decode(1, 1, -1)
+    with pytest.raises(lib.MflError):
+        lib.operand_matrix_offset(0, 0, 0, 0, 0, 0, 16, 2)
+    with pytest.raises(lib.MflError):
+        lib.operand_matrix_offset(0, 1, 0, 0, -1, 0, 16, 0)
+
+
 FAKE = 1 << 20  # a 16-byte aligned non-null value; never dereferenced (rejected first)
 
 
@@ -181,6 +285,14 @@ FAKE = 1 << 20  # a 16-byte aligned non-null value; never dereferenced (rejected
     (lambda m: m.acc_store_strided(0, FAKE, FAKE, 0, 8, 16), -2),
     (lambda m: m.acc_store_strided(1, FAKE, FAKE, (1 << 62), 0, 64), -2),
     (lambda m: m.mfma_probe(2, 0, FAKE, FAKE, None, FAKE), -1),
+    # strided operand load: contiguous extent past ld (both orders), int64 overflow, bad operand/order, odd pointer
+    (lambda m: m.operand_load_strided(0, 0, FAKE, 0, 1, 32, 0, FAKE), -2),
+    (lambda m: m.operand_load_strided(0, 1, FAKE, 1, 0, 32, 1, FAKE), -2),
+    (lambda m: m.operand_load_strided(1, 0, FAKE, 1 << 62, 0, 64, 0, FAKE), -2),
+    (lambda m: m.operand_load_strided(0, 2, FAKE, 0, 0, 64, 0, FAKE), -1),
+    (lambda m: m.operand_load_strided(0, 0, FAKE, 0, 0, 64, 2, FAKE), -1),
+    (lambda m: m.operand_load_strided(0, 0, FAKE + 1, 0, 0, 64, 0, FAKE), -1),
+    (lambda m: m.operand_load_strided(0, 0, FAKE, -1, 0, 64, 0, FAKE), -1),
 ])
 def test_device_entry_points_reject_bad_arguments(lib, call, status):
     with pytest.raises(lib.MflError) as e:

@@ -9,7 +9,7 @@ import torch
 import mma_fragment_layouts_amd as mfl
 from oracle import layouts as OL
 
-from _gpu import DT, device, host, say, stream
+from _gpu import DT, device, host, q16, say, stream
 
 pytestmark = pytest.mark.gpu
 
@@ -192,3 +192,86 @@ def test_mfma_accumulation_rounding(shape, fmt):
         report[name] = (got, models)
         assert models, f"{name}: {got!r} matches no model"
     print(f"mfma accumulation shape={shape} {fmt}:", report)
+
+
+# ---- operand fragments through the library (load-side twin of the strided store)
+
+OPNAME = {0: "A", 1: "B"}
+
+
+def _strided_host(rows, cols, row0, col0, ld, order, outer_pad, rng):
+    """A 16-bit matrix (as int16 bits) big enough for a rows x cols tile at
+    (row0, col0) in the given order, filled with random bits."""
+    outer = (row0 + rows if order == 0 else col0 + cols) + outer_pad
+    inner_need = (col0 + cols) if order == 0 else (row0 + rows)
+    assert inner_need <= ld
+    return rng.integers(-32768, 32768, (outer, ld)).astype(np.int16)
+
+
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("operand", [0, 1])
+@pytest.mark.parametrize("shape", [0, 1])
+def test_operand_load_strided_gathers_the_oracle_elements(shape, operand, order):
+    """Bit-exact: frag[lane*8 + i] is the matrix element the oracle's operand map
+    places at (lane, i), for random origins and leading dimensions."""
+    om = OL.OPERAND_MAPS[(shape, OPNAME[operand])]
+    rng = np.random.default_rng(300 + 4 * shape + 2 * operand + order)
+    for trial in range(3):
+        row0, col0 = int(rng.integers(0, 40)), int(rng.integers(0, 40))
+        inner = (col0 + om.cols) if order == 0 else (row0 + om.rows)
+        ld = inner + int(rng.integers(0, 24))
+        m = _strided_host(om.rows, om.cols, row0, col0, ld, order, 3, rng)
+        dm = torch.from_numpy(m).to(device())
+        frag = torch.empty(64 * 8, dtype=torch.int16, device=device())
+        say("operand load", shape, OPNAME[operand], order, row0, col0, ld)
+        mfl.operand_load_strided(shape, operand, dm, row0, col0, ld, order, frag, stream())
+        got = host(frag).reshape(64, 8)
+        flat = m.reshape(-1)
+        want = np.array([[flat[OL.operand_matrix_offset(om, l, i, row0, col0, ld, order)] for i in range(8)]
+                         for l in range(64)], np.int16)
+        assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("orders", [(0, 1), (1, 0), (0, 0), (1, 1)])
+@pytest.mark.parametrize("shape", [0, 1])
+def test_mma_through_library_layouts_matches_host_matmul(shape, orders, fmt):
+    """The whole register-level flow through the exported layouts: A and B tiles
+    gathered from strided matrices by operand_load_strided, one raw MFMA, the
+    accumulator scattered by acc_store_strided; exact against a host matmul of
+    small integers (exact in both 16-bit formats and in fp32)."""
+    fm, mn, k = GEOM[shape]
+    oa, ob = orders
+    rng = np.random.default_rng(400 + shape + 2 * oa + 4 * ob)
+    a = rng.integers(-8, 9, (mn, k)).astype(np.float32)
+    b = rng.integers(-8, 9, (k, mn)).astype(np.float32)
+    exact = a.astype(np.float64) @ b.astype(np.float64)
+
+    def embed(t, row0, col0, order):
+        rows, cols = t.shape
+        ld = (col0 + cols if order == 0 else row0 + rows) + 5
+        outer = (row0 + rows if order == 0 else col0 + cols) + 2
+        big = np.full((outer, ld), np.nan, np.float32)   # NaN outside the tile: any stray read shows
+        if order == 0:
+            big[row0:row0 + rows, col0:col0 + cols] = t
+        else:
+            big[col0:col0 + cols, row0:row0 + rows] = t.T
+        return big, ld
+
+    abig, lda = embed(a, 3, 9, oa)
+    bbig, ldb = embed(b, 6, 2, ob)
+    a16, b16 = q16(abig, fmt), q16(bbig, fmt)
+    af = torch.empty(512, dtype=torch.int16, device=device())
+    bf = torch.empty(512, dtype=torch.int16, device=device())
+    acc = torch.full((64 * fm.per_lane,), float("nan"), device=device())
+    say("library mma flow", shape, orders, fmt)
+    mfl.operand_load_strided(shape, mfl.OPERAND_A, a16, 3, 9, lda, oa, af, stream())
+    mfl.operand_load_strided(shape, mfl.OPERAND_B, b16, 6, 2, ldb, ob, bf, stream())
+    mfl.mfma_probe(shape, DT[fmt], af, bf, None, acc, stream())
+    ldc, row0, col0 = 2 * mn + 5, 4, mn + 1
+    c = torch.full((row0 + mn + 2, ldc), -3.0, device=device())
+    mfl.acc_store_strided(shape, acc, c, row0, col0, ldc, stream())
+    ch = host(c)
+    want = np.full(ch.shape, -3.0)
+    want[row0:row0 + mn, col0:col0 + mn] = exact
+    assert np.array_equal(ch, want)

@@ -151,3 +151,66 @@ def test_matrix_offset_overflow():
     assert big is not None and big < (1 << 63)
     with pytest.raises(ValueError):
         L.matrix_offset(fm, 0, 0, -1, 0, 16)
+
+
+# ---- operand fragments (the maps the device probe pins on hardware)
+
+@pytest.mark.parametrize("key", sorted(L.OPERAND_MAPS))
+def test_operand_maps_are_bijections_with_inverse(key):
+    om = L.OPERAND_MAPS[key]
+    assert L.operand_is_bijection(om)
+    inv = L.operand_decode_table(om)
+    assert sorted(inv) == list(range(om.rows * om.cols))
+    for o, (lane, i) in inv.items():
+        assert L.operand_offset(om, lane, i) == o
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+def test_operand_maps_are_transposes_of_each_other(shape):
+    """A and B of one instruction use the same lane assignment with row and column
+    exchanged: lane l supplies A[m][k] and B[k][m] for the same (m, k)."""
+    a, b = L.OPERAND_MAPS[(shape, "A")], L.OPERAND_MAPS[(shape, "B")]
+    for lane in range(64):
+        for i in range(8):
+            r, c = a.coords(lane, i)
+            assert b.coords(lane, i) == (c, r)
+            assert L.operand_offset(a, lane, i) == L.operand_offset(b, lane, i)
+
+
+@pytest.mark.parametrize("shape,mn,k", [(0, 16, 32), (1, 32, 16)])
+def test_operand_maps_cover_k_with_eight_consecutive_elements(shape, mn, k):
+    """Each lane's 8 elements are one row (A) of 8 consecutive K positions starting
+    at a multiple of 8: the 16-byte register group the MFMA reads."""
+    om = L.OPERAND_MAPS[(shape, "A")]
+    for lane in range(64):
+        pts = [om.coords(lane, i) for i in range(8)]
+        assert len({r for r, _ in pts}) == 1
+        ks = [c for _, c in pts]
+        assert ks == list(range(ks[0], ks[0] + 8)) and ks[0] % 8 == 0 and ks[-1] < k
+
+
+def test_operand_enumerator_catches_mutants():
+    om = L.OPERAND_MAPS[(0, "A")]
+
+    def mut(coords):
+        return L.OperandMap("mutant", "A", 64, 8, 16, 32, coords)
+
+    assert not L.operand_is_bijection(mut(lambda l, i: (l % 16, 8 * (l // 16) + (i & 6))))     # dropped i bit
+    assert not L.operand_is_bijection(mut(lambda l, i: (l % 16, 4 * (l // 16) + i)))           # wrong K stride
+    assert not L.operand_is_bijection(mut(lambda l, i: (8 * (l // 16) + i, l % 16)))           # transposed
+    swapped = mut(lambda l, i: (4 * (l % 4) + l // 16, 8 * ((l // 4) % 4) + i))                # lane digits swapped
+    assert L.operand_is_bijection(swapped)
+    assert any(swapped.coords(l, 0) != om.coords(l, 0) for l in range(64))
+
+
+def test_operand_matrix_offset_orders_and_overflow():
+    om = L.OPERAND_MAPS[(1, "B")]       # 16 x 32 (K x N)
+    r, c = om.coords(37, 5)
+    assert L.operand_matrix_offset(om, 37, 5, 3, 7, 100, 0) == (3 + r) * 100 + 7 + c
+    assert L.operand_matrix_offset(om, 37, 5, 3, 7, 100, 1) == (7 + c) * 100 + 3 + r
+    assert L.operand_matrix_offset(om, 63, 7, 0, 0, 32, 0) is not None
+    assert L.operand_matrix_offset(om, 63, 7, 0, 1, 32, 0) is None            # column spills past ld
+    assert L.operand_matrix_offset(om, 63, 7, 17, 0, 32, 1) is None           # row spills past ld (col-major)
+    assert L.operand_matrix_offset(om, 0, 0, 1 << 62, 0, 4, 0) is None        # int64 overflow
+    with pytest.raises(ValueError):
+        L.operand_matrix_offset(om, 0, 0, 0, 0, 16, 2)
