@@ -133,7 +133,9 @@ def gemm_256(torch, mfl, inputs, stream, dev, q16, out):
 
 
 def block_repeat(torch, mfl, inputs, stream, dev, q16, out):
-    """2048^2 output, 64 repeats."""
+    """2048^2 output, 64 repeats; both arms of the Warp spike's comparison: the
+    register accumulator with swizzled LDS and the shared-memory API (plain LDS
+    tiles, C through LDS on every repeat)."""
     rep = {}
     for tm, tn, tk, th in [(64, 64, 64, 64), (64, 64, 64, 128), (64, 64, 64, 256), (32, 32, 32, 128),
                            (128, 128, 32, 128), (128, 128, 32, 256)]:
@@ -142,8 +144,13 @@ def block_repeat(torch, mfl, inputs, stream, dev, q16, out):
             da, db = q16(a, dt), q16(bt, dt)
             c = torch.empty((2048, 2048), device=dev)
             ms = best_of(lambda: mfl.gemm_block_repeat(dt, tm, tn, tk, th, 64, 2048, 2048, da, db, c, stream), stream)
+            ms_lds = best_of(lambda: mfl.gemm_block_repeat_lds_api(dt, tm, tn, tk, th, 64, 2048, 2048, da, db, c,
+                                                                   stream), stream)
             tf = 2 * 2048 * 2048 * tk * 64 / ms / 1e9
-            rep[f"{tm}x{tn}x{tk}/{th}/{name}"] = {"tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            tf_lds = 2 * 2048 * 2048 * tk * 64 / ms_lds / 1e9
+            rep[f"{tm}x{tn}x{tk}/{th}/{name}"] = {"tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                                 "lds_api_tflops": round(tf_lds, 1),
+                                                 "register_over_lds_api": round(tf / tf_lds, 2)}
     out["block_repeat"] = rep
 
 

@@ -211,6 +211,17 @@ MFL_API int gemm_block_repeat(int dtype, int tm, int tn, int tk, int threads, in
                       int64_t m, int64_t n, const void *a, const void *b, float *c,
                       void *stream);
 
+/* The same workload through the other arm of Warp issue #1965's comparison,
+ * the shared-memory pointer API ("Description"): A and B in plain
+ * (unswizzled) LDS tiles, and C kept in an fp32 LDS tile that every repeat
+ * reads into registers, updates with one block MMA and writes back, with a
+ * workgroup barrier between repeats.  Same arguments, result, tiles and errors
+ * as gemm_block_repeat; it exists to measure the bank conflicts and the C
+ * round trip the issue attributes to that API. */
+MFL_API int gemm_block_repeat_lds_api(int dtype, int tm, int tn, int tk, int threads, int repeats,
+                      int64_t m, int64_t n, const void *a, const void *b, float *c,
+                      void *stream);
+
 /* Split-precision fp32 GEMM (Strata PR #800, "The fix"): A and B are fp32; an
  * operand in MFL_SPLIT mode is split on load into hi = RNE(x) and
  * lo = RNE(x - hi) of type `piece` (MFL_F16 or MFL_BF16), an operand in

@@ -49,6 +49,7 @@ _SIGNATURES = {
     "gemm_tile_mma_shape": (_i32, [_i32, _i32, _i64, _i64, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _vp, _i64,
                                    _i32, _vp]),
     "gemm_block_repeat": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "gemm_block_repeat_lds_api": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp]),
     "gemm_split_fp32": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _i64, _i32, _i32, _i32, _i32,
                                _vp, _i64, _i32, _vp]),
     "attention_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _pi64]),
@@ -228,6 +229,11 @@ def gemm_tile_mma_shape(shape, dtype, m, n, k, a, lda, order_a, b, ldb, order_b,
 def gemm_block_repeat(dtype, tm, tn, tk, threads, repeats, m, n, a, b, c, stream=None) -> None:
     _check(load().gemm_block_repeat(dtype, tm, tn, tk, threads, repeats, m, n, _ptr(a), _ptr(b), _ptr(c),
                                     _stream(stream)), "gemm_block_repeat")
+
+
+def gemm_block_repeat_lds_api(dtype, tm, tn, tk, threads, repeats, m, n, a, b, c, stream=None) -> None:
+    _check(load().gemm_block_repeat_lds_api(dtype, tm, tn, tk, threads, repeats, m, n, _ptr(a), _ptr(b), _ptr(c),
+                                            _stream(stream)), "gemm_block_repeat_lds_api")
 
 
 def gemm_split_fp32(piece, m, n, k, a, lda, order_a, mode_a, b, ldb, order_b, mode_b, chains, lolo, c, ldc,

@@ -90,6 +90,14 @@ struct FragOffsets {
   static_assert(operand_layout(SHAPE).rows == MN && operand_layout(SHAPE).cols == KM,
                 "fragment reads must follow the operand numeral of the instruction");
   int off[KSTEPS];
+  struct Plain {};
+  // Unswizzled rows (chunk c of a row at c*8): the plain LDS layout of the
+  // block-repeat ablation.
+  __device__ __forceinline__ FragOffsets(int row0, int lane, Plain) {
+    const int lr = lane % MN, lk = lane / MN;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) off[kk] = (row0 + lr) * BK + (kk * CPK + lk) * 8;
+  }
   __device__ __forceinline__ FragOffsets(int row0, int lane) {
     const int lr = lane % MN, lk = lane / MN;
 #pragma unroll

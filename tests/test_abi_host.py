@@ -263,6 +263,9 @@ FAKE = 1 << 20  # a 16-byte aligned non-null value; never dereferenced (rejected
     (lambda m: m.gemm_block_repeat(0, 64, 64, 64, 96, 64, 2048, 2048, FAKE, FAKE, FAKE), -3),
     (lambda m: m.gemm_block_repeat(0, 64, 64, 64, 128, 64, 2000, 2048, FAKE, FAKE, FAKE), -3),
     (lambda m: m.gemm_block_repeat(0, 64, 64, 64, 128, -1, 2048, 2048, FAKE, FAKE, FAKE), -1),
+    (lambda m: m.gemm_block_repeat_lds_api(0, 48, 48, 64, 128, 64, 2048, 2048, FAKE, FAKE, FAKE), -3),
+    (lambda m: m.gemm_block_repeat_lds_api(2, 64, 64, 64, 128, 64, 2048, 2048, FAKE, FAKE, FAKE), -1),
+    (lambda m: m.gemm_block_repeat_lds_api(0, 64, 64, 64, 128, 64, 2048, 2048, FAKE + 2, FAKE, FAKE), -1),
     # split: chains beyond the products, lo*lo without two split operands, bad mode, ld % 4
     (lambda m: m.gemm_split_fp32(1, 64, 64, 64, FAKE, 64, 0, 1, FAKE, 64, 1, 0, 3, 0, FAKE, 64), -1),
     (lambda m: m.gemm_split_fp32(1, 64, 64, 64, FAKE, 64, 0, 1, FAKE, 64, 1, 0, 1, 1, FAKE, 64), -1),
