@@ -239,6 +239,32 @@ MFL_API int gemm_split_fp32(int piece, int64_t m, int64_t n, int64_t k,
                     int chains, int lolo, float *c, int64_t ldc, int accumulate,
                     void *stream);
 
+/* Workspace for gemm_split_fp32_ws: the bytes of the four 16-bit planes
+ * (hi and lo of A and of B, each operand rows x ld, 256-byte aligned) when the
+ * planes path applies — both operands MFL_SPLIT, A row-major and B
+ * column-major, m % 128 == 0, n % 128 == 0, k % 64 == 0 (k > 0), lda % 8 == 0,
+ * ldb % 8 == 0 — and 0 otherwise (then gemm_split_fp32_ws runs the
+ * split-on-load kernel, which needs none).  MFL_EINVAL on NULL or unknown
+ * orders / modes, MFL_EOVERFLOW if the size does not fit int64. */
+MFL_API int gemm_split_fp32_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t lda, int order_a,
+                                            int mode_a, int64_t ldb, int order_b, int mode_b, int64_t ldc,
+                                            int64_t *bytes);
+
+/* gemm_split_fp32 with a caller workspace (device memory, 256-byte aligned,
+ * at least gemm_split_fp32_workspace_bytes; owned by the caller, contents
+ * overwritten): when the planes path applies, each operand is split once into
+ * hi and lo planes in the workspace (Strata PR #800, "What's going on": the hi
+ * and lo halves) and the GEMM streams the planes; otherwise it is exactly
+ * gemm_split_fp32 and the workspace is not touched.  Same arguments, result
+ * and errors as gemm_split_fp32, plus MFL_EINVAL for a missing, misaligned or
+ * short workspace.  The two kernels issue the same MFMAs in the same order per
+ * accumulator, so their results are bit-identical. */
+MFL_API int gemm_split_fp32_ws(int piece, int64_t m, int64_t n, int64_t k,
+                    const float *a, int64_t lda, int order_a, int mode_a,
+                    const float *b, int64_t ldb, int order_b, int mode_b,
+                    int chains, int lolo, float *c, int64_t ldc, int accumulate,
+                    void *workspace, int64_t workspace_bytes, void *stream);
+
 /* gemm_tile_mma with an explicit MFMA instruction for the fast path
  * (MFL_MFMA_16X16X32 or MFL_MFMA_32X32X16); gemm_tile_mma uses 16x16x32.  The
  * generic path (other orders, ragged sizes) always uses 16x16x32. */

@@ -52,6 +52,9 @@ _SIGNATURES = {
     "gemm_block_repeat_lds_api": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp]),
     "gemm_split_fp32": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _i64, _i32, _i32, _i32, _i32,
                                _vp, _i64, _i32, _vp]),
+    "gemm_split_fp32_workspace_bytes": (_i32, [_i64, _i64, _i64, _i64, _i32, _i32, _i64, _i32, _i32, _i64, _pi64]),
+    "gemm_split_fp32_ws": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _i64, _i32, _i32, _i32, _i32,
+                                  _vp, _i64, _i32, _vp, _i64, _vp]),
     "attention_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _pi64]),
     "attention_split_fp32": (_i32, [_i64, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i64, _vp]),
 }
@@ -240,6 +243,20 @@ def gemm_split_fp32(piece, m, n, k, a, lda, order_a, mode_a, b, ldb, order_b, mo
                     accumulate=0, stream=None) -> None:
     _check(load().gemm_split_fp32(piece, m, n, k, _ptr(a), lda, order_a, mode_a, _ptr(b), ldb, order_b, mode_b,
                                   chains, lolo, _ptr(c), ldc, accumulate, _stream(stream)), "gemm_split_fp32")
+
+
+def gemm_split_fp32_workspace_bytes(m, n, k, lda, order_a, mode_a, ldb, order_b, mode_b, ldc) -> int:
+    b = C.c_int64()
+    _check(load().gemm_split_fp32_workspace_bytes(m, n, k, lda, order_a, mode_a, ldb, order_b, mode_b, ldc,
+                                                  C.byref(b)), "gemm_split_fp32_workspace_bytes")
+    return b.value
+
+
+def gemm_split_fp32_ws(piece, m, n, k, a, lda, order_a, mode_a, b, ldb, order_b, mode_b, chains, lolo, c, ldc,
+                       accumulate, workspace, workspace_bytes, stream=None) -> None:
+    _check(load().gemm_split_fp32_ws(piece, m, n, k, _ptr(a), lda, order_a, mode_a, _ptr(b), ldb, order_b, mode_b,
+                                     chains, lolo, _ptr(c), ldc, accumulate, _ptr(workspace), workspace_bytes,
+                                     _stream(stream)), "gemm_split_fp32_ws")
 
 
 def attention_workspace_bytes(nq, nk, d, algo=1) -> int:

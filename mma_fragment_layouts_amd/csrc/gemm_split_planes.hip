@@ -1,0 +1,235 @@
+// Split-precision fp32 GEMM from pre-split 16-bit planes (Strata PR #800, "The
+// fix": hi and lo products in separate accumulator chains, added in plain fp32
+// at the end).
+//
+// The split-on-load kernel (gemm_split.hpp) converts every fp32 tile it loads,
+// so each element of A is split once per column tile of C (and each element of
+// B once per row tile): at 4096^3 that is 32 conversions per element and about
+// three vector instructions per MFMA.  Here each operand is split once into hi
+// and lo planes in HBM (one elementwise pass), and the GEMM streams the four
+// 16-bit planes with the direct-to-LDS buffer loads of the dense fast path.
+//
+// Tile: 128 x 128 x 64, 8 waves of 64 x 32 outputs (two per SIMD), so that
+// three chains of accumulators (96 registers) fit beside the operand fragments.
+// Per MFMA K step a wave reads 4 + 4 A fragments and 2 + 2 B fragments for 24
+// MFMAs.  For every accumulator the MFMAs arrive in the same order as in the
+// split-on-load kernel (K steps ascending; within one, hh, hl, lh, ll), and the
+// chains are summed the same way, so both kernels give bit-identical results.
+#include "gemm_split.hpp"
+
+namespace mfl {
+
+template <int N>
+__device__ __forceinline__ void planes_wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int DT, class P>
+__global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* __restrict__ Ah,
+                                                                const uint16_t* __restrict__ Al,
+                                                                const uint16_t* __restrict__ Bh,
+                                                                const uint16_t* __restrict__ Bl, float* __restrict__ C,
+                                                                uint32_t lda, uint32_t ldb, uint32_t ldc, int K,
+                                                                int tiles_m, int tiles_n, int accumulate) {
+  static_assert(P::SA && P::SB, "the planes path splits both operands");
+  constexpr int SHAPE = 0, BM = 128, BN = 128, BK = 64, WGM = 2, WGN = 4, NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int MN = Shape<SHAPE>::MN;
+  constexpr int TM = WM / MN, TN = WN / MN;
+  constexpr int PLANE = BM * BK;                   // one plane's slab (BM == BN), 16-bit elements
+  constexpr int STAGE = 4 * PLANE;                 // A_hi | A_lo | B_hi | B_lo
+  constexpr int PER = BM / 8 / NW;                 // 8-row wave loads per plane and wave
+  constexpr int LOADS = 4 * PER;
+  static_assert(PER * 8 * NW == BM && BM == BN, "plane rows must split into 8-row wave loads");
+  static_assert((NW % 2) == 0, "per-lane swizzle is load-invariant only for an even number of waves");
+  using Acc = typename Shape<SHAPE>::Acc;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
+
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, &tm, &tn);
+  const int row0 = tm * BM, col0 = tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr0 = (wave / WGN) * WM, wc0 = (wave % WGN) * WN;
+
+  const rsrc_t rah = make_rsrc(Ah + (int64_t)row0 * lda, (uint32_t)BM * lda * 2u);
+  const rsrc_t ral = make_rsrc(Al + (int64_t)row0 * lda, (uint32_t)BM * lda * 2u);
+  const rsrc_t rbh = make_rsrc(Bh + (int64_t)col0 * ldb, (uint32_t)BN * ldb * 2u);
+  const rsrc_t rbl = make_rsrc(Bl + (int64_t)col0 * ldb, (uint32_t)BN * ldb * 2u);
+  // Load i of this wave fills plane rows (i*NW + wave)*8 .. +8; lane l writes
+  // row +l/8, physical chunk l%8, fetching logical chunk (l%8) ^ swz(row).
+  const int lrow = wave * 8 + (lane >> 3);
+  const uint32_t va = (uint32_t)lrow * lda * 2u + (uint32_t)(((lane & 7) ^ swz<BK>(lrow)) << 4);
+  const uint32_t vb = (uint32_t)lrow * ldb * 2u + (uint32_t)(((lane & 7) ^ swz<BK>(lrow)) << 4);
+
+  auto issue = [&](int stage, int k0) {
+    uint16_t* base = lds + stage * STAGE + wave * 8 * BK;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t sa = (uint32_t)(i * NW * 8) * lda * 2u + (uint32_t)k0 * 2u;
+      const uint32_t sb = (uint32_t)(i * NW * 8) * ldb * 2u + (uint32_t)k0 * 2u;
+      uint16_t* dst = base + i * NW * 8 * BK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rah, (lds_ptr_t)(dst), 16, va, sa, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ral, (lds_ptr_t)(dst + PLANE), 16, va, sa, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbh, (lds_ptr_t)(dst + 2 * PLANE), 16, vb, sb, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbl, (lds_ptr_t)(dst + 3 * PLANE), 16, vb, sb, 0, 0);
+    }
+  };
+
+  const FragOffsets<SHAPE, BK> fa(wr0, lane), fb(wc0, lane);
+  Acc acc[P::CHAINS][TM][TN];
+#pragma unroll
+  for (int ch = 0; ch < P::CHAINS; ++ch) zero_acc<SHAPE, TM, TN>(acc[ch]);
+
+  const int KT = K / BK;
+  if (KT > 0) issue(0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    // this wave's loads of stage kt have landed; after the barrier every
+    // wave's have, and stage kt-1 (the buffer refilled next) is retired
+    planes_wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * BK);
+    const uint16_t* st = lds + (kt & 1) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < FragOffsets<SHAPE, BK>::KSTEPS; ++kk) {
+      u32x4 ah[TM], al[TM], bh[TN], bl[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        ah[i] = lds_read16(st, fa.off[kk] + i * MN * BK);
+        al[i] = lds_read16(st + PLANE, fa.off[kk] + i * MN * BK);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        bh[j] = lds_read16(st + 2 * PLANE, fb.off[kk] + j * MN * BK);
+        bl[j] = lds_read16(st + 3 * PLANE, fb.off[kk] + j * MN * BK);
+      }
+#pragma unroll
+      for (int p = 0; p < P::NPROD; ++p)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const u32x4 av = P::a_lo(p) ? al[i] : ah[i];
+            const u32x4 bv = P::b_lo(p) ? bl[j] : bh[j];
+            acc[P::chain(p)][i][j] = mfma<SHAPE, DT>(av, bv, acc[P::chain(p)][i][j]);
+          }
+    }
+  }
+  static_assert(LOADS < 64, "vmcnt range");
+  // Chains in plain fp32, the small ones first: c0 + (c1 + c2).
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (P::CHAINS == 3) acc[1][i][j] = acc[1][i][j] + acc[2][i][j];
+      if constexpr (P::CHAINS >= 2) acc[0][i][j] = acc[0][i][j] + acc[1][i][j];
+    }
+  const rsrc_t rc = make_rsrc(C + (int64_t)(row0 + wr0) * ldc + col0 + wc0, (uint32_t)WM * ldc * 4u);
+  if (accumulate)
+    store_acc_rsrc<SHAPE, TM, TN, true>(rc, ldc, lane, acc[0]);
+  else
+    store_acc_rsrc<SHAPE, TM, TN, false>(rc, ldc, lane, acc[0]);
+}
+
+template <int DT, class P>
+static int launch_planes(const uint16_t* ah, const uint16_t* al, const uint16_t* bh, const uint16_t* bl, float* c,
+                         int64_t lda, int64_t ldb, int64_t ldc, int M, int N, int K, int accumulate, hipStream_t s) {
+  const int tiles_m = M / 128, tiles_n = N / 128;
+  hipLaunchKernelGGL((gemm_split_planes_kernel<DT, P>), dim3(tiles_m * tiles_n), dim3(512), 0, s, ah, al, bh, bl, c,
+                     (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, K, tiles_m, tiles_n, accumulate);
+  return launch_status();
+}
+
+template <int DT>
+static int dispatch_planes(int chains, bool lolo, const uint16_t* ah, const uint16_t* al, const uint16_t* bh,
+                           const uint16_t* bl, float* c, int64_t lda, int64_t ldb, int64_t ldc, int M, int N, int K,
+                           int accumulate, hipStream_t s) {
+#define MFL_PLANES(CH, LL) \
+  return launch_planes<DT, Products<true, true, CH, LL>>(ah, al, bh, bl, c, lda, ldb, ldc, M, N, K, accumulate, s)
+  if (lolo) {
+    if (chains == 1) MFL_PLANES(1, true);
+    if (chains == 2) MFL_PLANES(2, true);
+    MFL_PLANES(3, true);
+  }
+  if (chains == 1) MFL_PLANES(1, false);
+  if (chains == 2) MFL_PLANES(2, false);
+  MFL_PLANES(3, false);
+#undef MFL_PLANES
+}
+
+static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+// Plane sizes: A as m rows of lda, B as n rows (columns of B) of ldb, 16-bit.
+static int64_t planes_bytes(int64_t m, int64_t n, int64_t lda, int64_t ldb) {
+  return 2 * align256(m * lda * 2) + 2 * align256(n * ldb * 2);
+}
+
+// The planes path takes both operands split and K contiguous, whole tiles, rows
+// of the planes 16-byte aligned, and 32-bit buffer offsets within a 128-row panel.
+static bool planes_apply(int64_t m, int64_t n, int64_t k, int64_t lda, int order_a, int mode_a, int64_t ldb,
+                         int order_b, int mode_b, int64_t ldc) {
+  const int64_t lim = (int64_t)1 << 32;
+  return mode_a == MFL_SPLIT && mode_b == MFL_SPLIT && order_a == MFL_ROW_MAJOR && order_b == MFL_COL_MAJOR &&
+         m % 128 == 0 && n % 128 == 0 && k % 64 == 0 && k > 0 && lda % 8 == 0 && ldb % 8 == 0 &&
+         128 * lda * 2 < lim && 128 * ldb * 2 < lim && 64 * ldc * 4 < lim;
+}
+
+}  // namespace mfl
+
+using namespace mfl;
+
+extern "C" int split_fp32(int dtype, const float* x, void* hi, void* lo, int64_t n, void* stream);
+
+extern "C" int gemm_split_fp32_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t lda, int order_a, int mode_a,
+                                               int64_t ldb, int order_b, int mode_b, int64_t ldc, int64_t* bytes) {
+  if (!bytes || m < 0 || n < 0 || k < 0 || lda < 0 || ldb < 0 || ldc < 0) return MFL_EINVAL;
+  if ((order_a != MFL_ROW_MAJOR && order_a != MFL_COL_MAJOR) || (order_b != MFL_ROW_MAJOR && order_b != MFL_COL_MAJOR))
+    return MFL_EINVAL;
+  if ((mode_a != MFL_ROUND && mode_a != MFL_SPLIT) || (mode_b != MFL_ROUND && mode_b != MFL_SPLIT)) return MFL_EINVAL;
+  if (!planes_apply(m, n, k, lda, order_a, mode_a, ldb, order_b, mode_b, ldc)) {
+    *bytes = 0;  // the split-on-load kernel runs; it needs no workspace
+    return MFL_OK;
+  }
+  if (m > INT64_MAX / 4 / lda || n > INT64_MAX / 4 / ldb) return MFL_EOVERFLOW;
+  *bytes = planes_bytes(m, n, lda, ldb);
+  return MFL_OK;
+}
+
+extern "C" int gemm_split_fp32(int piece, int64_t m, int64_t n, int64_t k, const float* a, int64_t lda, int order_a,
+                               int mode_a, const float* b, int64_t ldb, int order_b, int mode_b, int chains, int lolo,
+                               float* c, int64_t ldc, int accumulate, void* stream);
+
+extern "C" int gemm_split_fp32_ws(int piece, int64_t m, int64_t n, int64_t k, const float* a, int64_t lda, int order_a,
+                                  int mode_a, const float* b, int64_t ldb, int order_b, int mode_b, int chains,
+                                  int lolo, float* c, int64_t ldc, int accumulate, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+  if (!planes_apply(m, n, k, lda, order_a, mode_a, ldb, order_b, mode_b, ldc))
+    return gemm_split_fp32(piece, m, n, k, a, lda, order_a, mode_a, b, ldb, order_b, mode_b, chains, lolo, c, ldc,
+                           accumulate, stream);
+  // Same argument checks as gemm_split_fp32 for what the planes path can meet.
+  if (piece != MFL_F16 && piece != MFL_BF16) return MFL_EINVAL;
+  if ((lolo != 0 && lolo != 1) || (accumulate != 0 && accumulate != 1)) return MFL_EINVAL;
+  if (chains < 1 || chains > 3 || chains > 3 + lolo) return MFL_EINVAL;
+  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return MFL_EUNSUPPORTED;
+  if (!a || !b || !c || !aligned16(a) || !aligned16(b) || ((uintptr_t)c & 3)) return MFL_EINVAL;
+  if (lda < k || ldb < k || ldc < n) return MFL_EINVAL;
+  if (m > INT64_MAX / 4 / lda || n > INT64_MAX / 4 / ldb || m > INT64_MAX / ldc) return MFL_EOVERFLOW;
+  if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < planes_bytes(m, n, lda, ldb)) return MFL_EINVAL;
+  char* w = (char*)workspace;
+  uint16_t* ah = (uint16_t*)w;
+  uint16_t* al = (uint16_t*)(w + align256(m * lda * 2));
+  uint16_t* bh = (uint16_t*)(w + 2 * align256(m * lda * 2));
+  uint16_t* bl = (uint16_t*)(w + 2 * align256(m * lda * 2) + align256(n * ldb * 2));
+  // Split exactly the elements an m x k (n x k) operand with that leading
+  // dimension spans, (rows - 1) * ld + k: the last row need not be padded.
+  int st;
+  if ((st = split_fp32(piece, a, ah, al, (m - 1) * lda + k, stream)) != MFL_OK) return st;
+  if ((st = split_fp32(piece, b, bh, bl, (n - 1) * ldb + k, stream)) != MFL_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (piece == MFL_BF16)
+    return dispatch_planes<MFL_BF16>(chains, lolo, ah, al, bh, bl, c, lda, ldb, ldc, (int)m, (int)n, (int)k,
+                                     accumulate, s);
+  return dispatch_planes<MFL_F16>(chains, lolo, ah, al, bh, bl, c, lda, ldb, ldc, (int)m, (int)n, (int)k, accumulate,
+                                  s);
+}

@@ -312,6 +312,33 @@ def test_empty_problems_are_noops_without_a_device(lib):
     lib.quantize_fp32(1, FAKE, FAKE, 0)
 
 
+def test_split_planes_workspace_size(lib):
+    R_, C_, S_, Rd = lib.ROW_MAJOR, lib.COL_MAJOR, lib.SPLIT, lib.ROUND
+    al = lambda x: (x + 255) // 256 * 256
+    # applicable: four 16-bit planes, each operand rows x ld, 256-aligned
+    assert lib.gemm_split_fp32_workspace_bytes(512, 384, 640, 648, R_, S_, 664, C_, S_, 384) == \
+        2 * al(512 * 648 * 2) + 2 * al(384 * 664 * 2)
+    # not applicable: no workspace (the split-on-load kernel runs)
+    for args in [(512, 384, 640, 648, R_, Rd, 664, C_, S_, 384),   # A rounded
+                 (512, 384, 640, 648, C_, S_, 664, C_, S_, 384),   # A K-strided
+                 (500, 384, 640, 648, R_, S_, 664, C_, S_, 384),   # M % 128
+                 (512, 384, 600, 648, R_, S_, 664, C_, S_, 384),   # K % 64
+                 (512, 384, 640, 644, R_, S_, 664, C_, S_, 384)]:  # lda % 8
+        assert lib.gemm_split_fp32_workspace_bytes(*args) == 0
+    with pytest.raises(lib.MflError):
+        lib.gemm_split_fp32_workspace_bytes(512, 384, 640, 648, 2, S_, 664, C_, S_, 384)
+    with pytest.raises(lib.MflError):
+        lib.gemm_split_fp32_workspace_bytes(512, 384, 640, 648, R_, 3, 664, C_, S_, 384)
+
+
+@pytest.mark.parametrize("ws,wsb", [(FAKE, 1024), (0, 1 << 40), (FAKE + 16, 1 << 40)])
+def test_split_planes_rejects_bad_workspace(lib, ws, wsb):
+    with pytest.raises(lib.MflError) as e:
+        lib.gemm_split_fp32_ws(1, 512, 384, 640, FAKE, 648, lib.ROW_MAJOR, lib.SPLIT, FAKE, 664, lib.COL_MAJOR,
+                               lib.SPLIT, 3, 0, FAKE, 384, 0, ws, wsb)
+    assert e.value.status == lib.EINVAL
+
+
 def test_attention_workspace_size(lib):
     b = lib.attention_workspace_bytes(2048, 32768, 128, 0)
     assert b >= 2048 * 32768 * 4 + 2 * 2048 * 4 + 2048 * 128 * 4

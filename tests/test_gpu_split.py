@@ -119,3 +119,69 @@ def test_split_full_size_sampled():
     assert errs[(3, 0)] <= 5e-6
     assert errs[(2, 0)] <= 5e-6
     assert errs[(3, 1)] <= 5e-6
+
+
+# ---- planes path (gemm_split_fp32_ws): operands split once into hi / lo planes
+
+def run_both(a, bt, chains, lolo, piece, accumulate=0, seed=0):
+    """The same product through gemm_split_fp32 (split on load) and
+    gemm_split_fp32_ws (planes); leading dimensions padded with NaN and
+    different for A and B; C preset to random values when accumulating."""
+    m, k = a.shape
+    n = bt.shape[0]
+    lda, ldb = k + (-k) % 8 + 8, k + (-k) % 8 + 24
+    da, db = dev32(padded(a, lda)), dev32(padded(bt, ldb))
+    wsb = mfl.gemm_split_fp32_workspace_bytes(m, n, k, lda, mfl.ROW_MAJOR, mfl.SPLIT, ldb, mfl.COL_MAJOR, mfl.SPLIT, n)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=device())
+    c0 = np.random.default_rng(seed).standard_normal((m, n)).astype(np.float32) if accumulate else \
+        np.full((m, n), np.nan, np.float32)
+    c_load, c_planes = dev32(c0), dev32(c0)
+    mfl.gemm_split_fp32(DT[piece], m, n, k, da, lda, mfl.ROW_MAJOR, mfl.SPLIT, db, ldb, mfl.COL_MAJOR, mfl.SPLIT,
+                        chains, lolo, c_load, n, accumulate, stream())
+    mfl.gemm_split_fp32_ws(DT[piece], m, n, k, da, lda, mfl.ROW_MAJOR, mfl.SPLIT, db, ldb, mfl.COL_MAJOR, mfl.SPLIT,
+                           chains, lolo, c_planes, n, accumulate, ws, wsb, stream())
+    return host(c_load), host(c_planes), wsb
+
+
+@pytest.mark.parametrize("accumulate", [0, 1])
+@pytest.mark.parametrize("piece", ["bf16", "f16"])
+@pytest.mark.parametrize("chains,lolo", [(1, 0), (2, 0), (3, 0), (1, 1), (2, 1), (3, 1)])
+def test_split_planes_bit_identical_to_split_on_load(chains, lolo, piece, accumulate):
+    """Both kernels issue the same MFMAs in the same order per accumulator and
+    sum the chains the same way: the results must agree bit for bit."""
+    a, bt = inputs.gemm_split(512, 384, 640)
+    say("split planes vs on-load", chains, lolo, piece, accumulate)
+    c_load, c_planes, wsb = run_both(a, bt, chains, lolo, piece, accumulate, seed=chains + 4 * lolo)
+    assert wsb > 0
+    assert not np.isnan(c_planes).any()
+    assert np.array_equal(c_load.view(np.uint32), c_planes.view(np.uint32))
+
+
+@pytest.mark.parametrize("chains", [2, 3])
+def test_split_planes_against_oracle(medium, chains):
+    a, bt, ref, exp3, _ = medium
+    say("split planes oracle", chains)
+    _, c, _ = run_both(a, bt, chains, 0, "bf16")
+    assert R.rel_error(c, ref) <= 5e-6
+    assert R.rel_error(c, exp3) <= 2e-6
+
+
+def test_split_planes_not_applicable_falls_back():
+    """M not a multiple of 128: no workspace is needed and the call is the
+    split-on-load kernel (identical result)."""
+    a, bt = inputs.gemm_split(200, 384, 640)
+    say("split planes fallback")
+    c_load, c_ws, wsb = run_both(a, bt, 3, 0, "bf16")
+    assert wsb == 0
+    assert np.array_equal(c_load.view(np.uint32), c_ws.view(np.uint32))
+
+
+def test_split_planes_full_size_bit_identical():
+    """M = N = K = 4096 with outliers, chains 3 and 1: whole C bit-identical to
+    the split-on-load kernel (whose sampled rows the oracle checks above)."""
+    a, bt = inputs.gemm_split()
+    for chains in (3, 1):
+        say("split planes 4096^3", chains)
+        c_load, c_planes, wsb = run_both(a, bt, chains, 0, "bf16")
+        assert wsb > 0
+        assert np.array_equal(c_load.view(np.uint32), c_planes.view(np.uint32))
