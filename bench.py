@@ -78,9 +78,20 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(a, bt):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(a, bt, budget_s=10.0, max_runs=20):
     """The oracle as it stands (numpy fp64 on the quantised inputs), timed on the
-    host's cores over the full 4096^3 problem."""
+    host's cores over the full 4096^3 problem, repeated for about budget_s
+    seconds; the median run is reported."""
     from oracle import reference as R
     try:
         from threadpoolctl import threadpool_info
@@ -88,12 +99,50 @@ def cpu_baseline(a, bt):
                       default=1)
     except Exception:
         threads = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    R.gemm_ref(a[:, :4096], bt[:, :4096], "bf16")
-    dt = time.perf_counter() - t0
+    runs = []
+    start = time.perf_counter()
+    while len(runs) < max_runs and (not runs or time.perf_counter() - start < budget_s):
+        t0 = time.perf_counter()
+        R.gemm_ref(a[:, :4096], bt[:, :4096], "bf16")
+        runs.append(time.perf_counter() - t0)
+    dt = float(np.median(runs))
     return {"value": 2 * 4096 ** 3 / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": "full 4096^3 bf16 GEMM: RNE quantisation of A and B plus the fp64 matmul, one run",
-            "seconds": round(dt, 3)}
+            "sample": f"full 4096^3 bf16 GEMM (RNE quantisation of A and B plus the fp64 matmul), median of "
+                      f"{len(runs)} runs in {time.perf_counter() - start:.1f} s",
+            "seconds": round(dt, 3), "cpu_model": cpu_model(), "nproc": os.cpu_count()}
+
+
+def sclk_under_load(step, torch, seconds=1.0):
+    """SCLK (MHz) read by rocm-smi, run as a child process, while the GEMM runs
+    back to back; None if the tool or its output is unavailable."""
+    import re
+    import subprocess
+    import threading
+    found = {}
+
+    def probe():
+        time.sleep(seconds / 2)
+        try:
+            out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                                 timeout=30).stdout
+            for card in json.loads(out).values():
+                for key, val in card.items():
+                    if key.lower().startswith("sclk"):
+                        m = re.search(r"(\d+)\s*mhz", str(val), re.I)
+                        if m:
+                            found["mhz"] = int(m.group(1))
+        except Exception:
+            pass
+
+    th = threading.Thread(target=probe)
+    th.start()
+    t0 = time.perf_counter()
+    while th.is_alive() and time.perf_counter() - t0 < 60:
+        for _ in range(50):
+            step()
+        torch.cuda.synchronize()
+    th.join()
+    return found.get("mhz")
 
 
 EXTRA = ("gemm_256", "block_repeat", "split", "attention")
@@ -209,6 +258,7 @@ def main():
     p.add_argument("--extra", default=",".join(EXTRA),
                    help="comma list of the other workloads to run (" + ", ".join(EXTRA) + ")")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-clock", action="store_true", help="skip the SCLK reading under load")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run 3 plain device copies of 256 MiB (reference for the HBM byte counters)")
     args = p.parse_args()
@@ -287,6 +337,9 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
     }
+    if not args.no_clock:
+        log("clock under load")
+        result["roofline"]["sclk_mhz_under_load"] = sclk_under_load(step, torch)
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
