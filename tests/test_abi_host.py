@@ -349,3 +349,22 @@ def test_attention_workspace_size(lib):
         lib.attention_workspace_bytes(2048, 32768, 96, 1)
     with pytest.raises(lib.MflError):
         lib.attention_workspace_bytes(2048, 32768, 128, 5)
+
+
+def test_plain_c_program_uses_the_header_and_library(tmp_path):
+    """include/mfl.h is valid C99 (pedantic, warnings as errors) and the host
+    calls work from a C program linked against libmfl.so (tests/c)."""
+    import shutil
+    import subprocess
+    from mma_fragment_layouts_amd import _binding
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler on this host")
+    libdir = os.path.dirname(_binding.LIB_PATH)
+    exe = tmp_path / "abi_host_check"
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c", "abi_host_check.c"), "-L", libdir, "-lmfl",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True, capture_output=True, text=True)
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stderr
+    assert "ok" in run.stdout
