@@ -103,14 +103,18 @@ def softmax_rows(s):
     return pt, m[:, 0], pt.sum(axis=1)
 
 
-def attention_ref(q, k, v, fmt: str = "f16") -> np.ndarray:
+def attention_ref(q, k, v, fmt: str = "f16", round_kv: bool = True) -> np.ndarray:
     """O = softmax(Q @ Q16(K)^T) @ Q16(V) in fp64, with Q at its original fp32
     values and K, V rounded once to ``fmt`` (Strata PR #800: only q and p are
     split; the pages state neither a causal mask nor a 1/sqrt(d) scale, so there
-    is none)."""
-    s = matmul_f64(q, quantize(k, fmt))
+    is none).  round_kv=False keeps K and V at their original fp32 values too:
+    the reference of the variant that splits K and V as well, where every
+    operand is carried at fp32-input accuracy."""
+    kk = quantize(k, fmt) if round_kv else _f64(k)
+    vv = quantize(v, fmt) if round_kv else _f64(v)
+    s = matmul_f64(q, kk)
     pt, _, l = softmax_rows(s)
-    return (pt / l[:, None]) @ quantize(v, fmt)
+    return (pt / l[:, None]) @ vv
 
 
 def rel_error(c, r) -> float:

@@ -167,6 +167,28 @@ def test_attention_brute_force_tiny():
     assert np.allclose(R.attention_ref(q, k, v), out, rtol=1e-13)
 
 
+def test_attention_unrounded_kv():
+    """round_kv=False: K and V enter at their fp32 values.  Pinned by (1) equality
+    with the rounded reference when K and V are exactly representable in fp16,
+    (2) the Q = 0 closed form (column means of V itself), (3) brute force."""
+    rng = np.random.default_rng(9)
+    nk, d = 48, 8
+    k16 = F.quantize(rng.standard_normal((nk, d)).astype(np.float32), "f16").astype(np.float32)
+    v16 = F.quantize(rng.standard_normal((nk, d)).astype(np.float32), "f16").astype(np.float32)
+    q = rng.standard_normal((5, d)).astype(np.float32)
+    assert np.array_equal(R.attention_ref(q, k16, v16, round_kv=False), R.attention_ref(q, k16, v16))
+    v = (rng.standard_normal((nk, d)) * (1 + 2.0 ** -13)).astype(np.float32)   # not fp16-representable
+    o = R.attention_ref(np.zeros((2, d), np.float32), k16, v, round_kv=False)
+    assert np.allclose(o, np.tile(v.astype(np.float64).mean(axis=0), (2, 1)), rtol=1e-13, atol=1e-15)
+    assert not np.allclose(o, R.attention_ref(np.zeros((2, d), np.float32), k16, v), rtol=1e-9, atol=0)
+    k = rng.standard_normal((3, 2)).astype(np.float32)
+    vv = rng.standard_normal((3, 2)).astype(np.float32)
+    qq = rng.standard_normal((1, 2)).astype(np.float32)
+    w = [math.exp(float(qq[0, 0]) * float(k[j, 0]) + float(qq[0, 1]) * float(k[j, 1])) for j in range(3)]
+    out = [sum(w[j] * float(vv[j, c]) for j in range(3)) / sum(w) for c in range(2)]
+    assert np.allclose(R.attention_ref(qq, k, vv, round_kv=False)[0], out, rtol=1e-13)
+
+
 def test_rel_error_closed_form():
     r = np.arange(1, 10, dtype=np.float64).reshape(3, 3)
     assert math.isclose(R.rel_error(r * (1 + 1e-6), r), 1e-6, rel_tol=1e-9)
