@@ -235,13 +235,15 @@ def attention(torch, mfl, inputs, stream, dev, out):
     dq, dk, dv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
     o = torch.empty((2048, 128), device=dev)
     att = {}
-    for algo, aname in ((mfl.ATTN_MATERIALISED, "materialised"), (mfl.ATTN_FUSED, "fused")):
+    for algo, aname in ((mfl.ATTN_MATERIALISED, "materialised"), (mfl.ATTN_FUSED, "fused"),
+                        (mfl.ATTN_FUSED_SPLIT_KV, "fused_split_kv")):
         wsb = mfl.attention_workspace_bytes(2048, 32768, 128, algo)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        nprod = 3 if algo == mfl.ATTN_FUSED_SPLIT_KV else 2   # products per GEMM: hh, hl (, lh)
         for chains in (1, 2):
             ms = best_of(lambda: mfl.attention_split_fp32(2048, 32768, 128, dq, dk, dv, chains, algo, o, ws, wsb,
                                                           stream), stream, rounds=2, per=5)
-            mf = 2 * 2 * 2 * 2048 * 32768 * 128 / ms / 1e9   # 2 GEMMs x 2 products (hi, lo)
+            mf = 2 * nprod * 2 * 2048 * 32768 * 128 / ms / 1e9   # 2 GEMMs x nprod products
             att[f"{aname}_chains{chains}"] = {"ms": round(ms, 4), "mfma_tflops": round(mf, 1),
                                               "frac_mfma_peak": round(mf / PEAK_BF16_TFLOPS, 4)}
         del ws

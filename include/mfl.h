@@ -288,7 +288,11 @@ MFL_API int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int alg
  *           workspace (split GEMM, row softmax, split-K split GEMM, reduce);
  *   algo 1: fused — per 128 queries and key slice, both products and an online
  *           softmax (running max, rescaled accumulators) stay in registers and
- *           LDS; key slices are merged by their exp(m_s - m) weights.
+ *           LDS; key slices are merged by their exp(m_s - m) weights;
+ *   algo 2: fused, and K and V are split into f16 hi/lo as well (each product
+ *           then has the three terms hi*hi, hi*lo, lo*hi; with chains = 2 the
+ *           two corrections share the second chain), so every operand enters
+ *           at fp32-input accuracy instead of K and V being rounded once.
  * Supported: d = 128, nq and nk multiples of 128.  `workspace` is device memory
  * of at least attention_workspace_bytes(..., algo) bytes, 256-byte aligned. */
 MFL_API int attention_split_fp32(int64_t nq, int64_t nk, int64_t d, const float *q, const float *k,

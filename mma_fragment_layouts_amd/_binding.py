@@ -21,7 +21,7 @@ MFMA_16X16X32, MFMA_32X32X16 = 0, 1
 F16, BF16 = 0, 1
 ROW_MAJOR, COL_MAJOR = 0, 1
 ROUND, SPLIT = 0, 1
-ATTN_MATERIALISED, ATTN_FUSED = 0, 1
+ATTN_MATERIALISED, ATTN_FUSED, ATTN_FUSED_SPLIT_KV = 0, 1, 2
 OPERAND_A, OPERAND_B = 0, 1
 
 _i32, _i64, _vp = C.c_int, C.c_int64, C.c_void_p

@@ -19,9 +19,9 @@
 
 namespace mfl {
 
-int64_t attn_fused_workspace(int64_t nq, int64_t nk);
-int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, const float* v, int chains, float* o,
-                      void* workspace, hipStream_t st);
+int64_t attn_fused_workspace(int64_t nq, int64_t nk, bool skv);
+int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, const float* v, int chains, bool skv,
+                      float* o, void* workspace, hipStream_t st);
 
 namespace {
 
@@ -176,9 +176,9 @@ bool valid_sizes(int64_t nq, int64_t nk, int64_t d) {
 using namespace mfl;
 
 extern "C" int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int algo, int64_t* bytes) {
-  if (!bytes || (algo != 0 && algo != 1)) return MFL_EINVAL;
+  if (!bytes || algo < 0 || algo > 2) return MFL_EINVAL;
   if (!valid_sizes(nq, nk, d)) return MFL_EUNSUPPORTED;
-  *bytes = algo == 0 ? plan(nq, nk, d).total : attn_fused_workspace(nq, nk);
+  *bytes = algo == 0 ? plan(nq, nk, d).total : attn_fused_workspace(nq, nk, algo == 2);
   return MFL_OK;
 }
 
@@ -186,15 +186,16 @@ extern "C" int attention_split_fp32(int64_t nq, int64_t nk, int64_t d, const flo
                                     int chains, int algo, float* o, void* workspace, int64_t workspace_bytes,
                                     void* stream) {
   if (chains != 1 && chains != 2) return MFL_EINVAL;
-  if (algo != 0 && algo != 1) return MFL_EINVAL;
+  if (algo < 0 || algo > 2) return MFL_EINVAL;
   if (!valid_sizes(nq, nk, d)) return nq < 0 || nk < 0 || d < 0 ? MFL_EINVAL : MFL_EUNSUPPORTED;
   if (!q || !k || !v || !o || !workspace) return MFL_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MFL_EINVAL;
   if (((uintptr_t)workspace & 255) != 0) return MFL_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  if (algo == 1) {
-    if (workspace_bytes < attn_fused_workspace(nq, nk)) return MFL_EINVAL;
-    return launch_attn_fused(nq, nk, q, k, v, chains, o, workspace, s);
+  if (algo >= 1) {
+    const bool skv = algo == 2;
+    if (workspace_bytes < attn_fused_workspace(nq, nk, skv)) return MFL_EINVAL;
+    return launch_attn_fused(nq, nk, q, k, v, chains, skv, o, workspace, s);
   }
   const Workspace w = plan(nq, nk, d);
   if (workspace_bytes < w.total) return MFL_EINVAL;

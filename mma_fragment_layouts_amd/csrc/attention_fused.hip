@@ -11,37 +11,6 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// One workgroup per 32-key block (256 threads):
-//   K (nk x 128 fp32) -> K16 (nk x 128 fp16, round to nearest even);
-//   V (nk x 128 fp32) -> V16^T (128 x nk fp16), the keys of each 32-key block
-//   stored at vt_key_pos(r).  Thread (dim, half) gathers the 16 keys of
-//   storage positions 16 half .. 16 half + 15 for one dim: a wave's 64 lanes
-//   read 64 consecutive dims of one key per load.
-__global__ __launch_bounds__(256) void attn_prep(const float* __restrict__ K, const float* __restrict__ V,
-                                                 uint16_t* __restrict__ Kq, uint16_t* __restrict__ Vt, int nk) {
-  const int blk = blockIdx.x, t = threadIdx.x;
-  const int64_t base = (int64_t)blk * 32 * kAttnD;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int idx = (r * 256 + t) * 4;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(K + base + idx);
-    uint32_t w[2];
-    w[0] = pack2(to16<MFL_F16>(x[0]), to16<MFL_F16>(x[1]));
-    w[1] = pack2(to16<MFL_F16>(x[2]), to16<MFL_F16>(x[3]));
-    __builtin_memcpy(Kq + base + idx, w, 8);
-  }
-  const int dim = t & (kAttnD - 1), half = t >> 7;
-  uint16_t h[16];
-#pragma unroll
-  for (int p = 0; p < 16; ++p) h[p] = to16<MFL_F16>(V[base + (int64_t)vt_pos_key(16 * half + p) * kAttnD + dim]);
-  u32x4 o0, o1;
-  __builtin_memcpy(&o0, h, 16);
-  __builtin_memcpy(&o1, h + 8, 16);
-  uint16_t* dst = Vt + (int64_t)dim * nk + (int64_t)blk * 32 + 16 * half;
-  *reinterpret_cast<u32x4*>(dst) = o0;
-  *reinterpret_cast<u32x4*>(dst + 8) = o1;
-}
-
 // Packed hi/lo split of two fp32 values into fp16 pairs: hi = RNE16(x),
 // lo = RNE16(x - hi), with x - hi exact in fp32.
 struct Split2 {
@@ -52,6 +21,54 @@ __device__ __forceinline__ Split2 split2(float a, float b) {
   const f32x2 hf = __builtin_convertvector(h, f32x2);
   const h16x2 l = __builtin_convertvector(f32x2{a - hf.x, b - hf.y}, h16x2);
   return {__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};
+}
+
+// One workgroup per 32-key block (256 threads):
+//   K (nk x 128 fp32) -> K16 (nk x 128 fp16, round to nearest even);
+//   V (nk x 128 fp32) -> V16^T (128 x nk fp16), the keys of each 32-key block
+//   stored at vt_key_pos(r).  Thread (dim, half) gathers the 16 keys of
+//   storage positions 16 half .. 16 half + 15 for one dim: a wave's 64 lanes
+//   read 64 consecutive dims of one key per load.
+// SKV: K and V are split as well — K16 and V16^T hold the hi parts and Kl and
+// Vtl (same layouts) the lo parts, lo = RNE16(x - hi).
+template <bool SKV>
+__global__ __launch_bounds__(256) void attn_prep(const float* __restrict__ K, const float* __restrict__ V,
+                                                 uint16_t* __restrict__ Kq, uint16_t* __restrict__ Vt,
+                                                 uint16_t* __restrict__ Kl, uint16_t* __restrict__ Vtl, int nk) {
+  const int blk = blockIdx.x, t = threadIdx.x;
+  const int64_t base = (int64_t)blk * 32 * kAttnD;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int idx = (r * 256 + t) * 4;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(K + base + idx);
+    const Split2 a = split2(x[0], x[1]), b = split2(x[2], x[3]);
+    const uint32_t wh[2] = {a.hi, b.hi};
+    __builtin_memcpy(Kq + base + idx, wh, 8);
+    if constexpr (SKV) {
+      const uint32_t wl[2] = {a.lo, b.lo};
+      __builtin_memcpy(Kl + base + idx, wl, 8);
+    }
+  }
+  const int dim = t & (kAttnD - 1), half = t >> 7;
+  uint16_t h[16], l[16];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const float x = V[base + (int64_t)vt_pos_key(16 * half + p) * kAttnD + dim];
+    h[p] = to16<MFL_F16>(x);
+    if constexpr (SKV) l[p] = to16<MFL_F16>(x - from16<MFL_F16>(h[p]));
+  }
+  const int64_t doff = (int64_t)dim * nk + (int64_t)blk * 32 + 16 * half;
+  u32x4 o0, o1;
+  __builtin_memcpy(&o0, h, 16);
+  __builtin_memcpy(&o1, h + 8, 16);
+  *reinterpret_cast<u32x4*>(Vt + doff) = o0;
+  *reinterpret_cast<u32x4*>(Vt + doff + 8) = o1;
+  if constexpr (SKV) {
+    __builtin_memcpy(&o0, l, 16);
+    __builtin_memcpy(&o1, l + 8, 16);
+    *reinterpret_cast<u32x4*>(Vtl + doff) = o0;
+    *reinterpret_cast<u32x4*>(Vtl + doff + 8) = o1;
+  }
 }
 
 // Workgroup -> (query block, key slice).  With xcd_map the workgroups that an
@@ -72,16 +89,24 @@ __device__ __forceinline__ void attn_block_of(int b, int nwg, int qblocks, int x
 // is skipped for most chunks.  Any reference gives the same O = sum P~ V / sum P~
 // in real arithmetic.
 //
-template <int CHAINS, int STAGES>
+//
+// SKV: K and V are split too (hi planes Kq / Vt, lo planes Kl / Vtl).  A stage
+// then holds the lo tiles after the hi ones, and each GEMM adds the third
+// product into the correction chain: S = Kh Qh | (Kh Ql + Kl Qh), O += Vh Ph |
+// (Vh Pl + Vl Ph).
+template <int CHAINS, int STAGES, bool SKV>
 __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict__ Q, const uint16_t* __restrict__ Kq,
-                                                         const uint16_t* __restrict__ Vt, float* __restrict__ Opart,
+                                                         const uint16_t* __restrict__ Vt,
+                                                         const uint16_t* __restrict__ Kl,
+                                                         const uint16_t* __restrict__ Vtl, float* __restrict__ Opart,
                                                          float* __restrict__ Mpart, float* __restrict__ Lpart, int nq,
                                                          int nk, int keys_per_split, int qblocks, int xcd_map) {
   static_assert(kAttnQ == 128 && kAttnKV == 64 && kAttnD == 128, "tiling below assumes 128 x 64 x 128");
   static_assert(STAGES >= 2, "at least double buffering");
   constexpr int BK = 64;                    // LDS tile depth (dims for K16, keys for V16^T)
   constexpr int KT = kAttnKV * BK;          // one K16 half tile: 64 keys x 64 dims
-  constexpr int STAGE = 2 * KT + kAttnD * kAttnKV;  // K16 halves + V16^T tile (elements)
+  constexpr int HALF = 2 * KT + kAttnD * kAttnKV;  // K16 halves + V16^T tile (elements)
+  constexpr int STAGE = SKV ? 2 * HALF : HALF;     // hi tiles, then (SKV) lo tiles
   constexpr int NW = 8;                     // waves per workgroup, 16 queries each
   constexpr int LOADS = 32 / NW;            // 1 KiB wave loads per stage per wave
   __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE];
@@ -120,6 +145,8 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
   // 8*blk + lane/8 receives logical chunk (lane%8) ^ swz(row).
   const rsrc_t rk = make_rsrc(Kq, (uint32_t)((int64_t)nk * kAttnD * 2));
   const rsrc_t rv = make_rsrc(Vt, (uint32_t)((int64_t)nk * kAttnD * 2));
+  const rsrc_t rkl = make_rsrc(SKV ? Kl : Kq, (uint32_t)((int64_t)nk * kAttnD * 2));
+  const rsrc_t rvl = make_rsrc(SKV ? Vtl : Vt, (uint32_t)((int64_t)nk * kAttnD * 2));
   uint32_t voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
@@ -135,17 +162,22 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
   // With 8 waves, wave loads 0-1 (b = wave, wave + 8) fill K16 and 2-3 fill V16^T.
   static_assert(NW == 8 && LOADS == 4, "K16 / V16^T split of the wave loads assumes 8 waves");
   auto issue = [&](int chunk) {
-    uint16_t* base = lds + (chunk % STAGES) * STAGE;
     const uint32_t key0 = (uint32_t)(kbeg + chunk * kAttnKV);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int b = wave + NW * i;
-      if (i < 2)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(base + i * KT + wave * 8 * BK), 16, voff[i],
-                                                 key0 * kAttnD * 2u, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(base + 2 * KT + (b - 16) * 8 * BK), 16, voff[i],
-                                                 key0 * 2u, 0, 0);
+    for (int set = 0; set < (SKV ? 2 : 1); ++set) {
+      uint16_t* base = lds + (chunk % STAGES) * STAGE + set * HALF;
+      const rsrc_t& rks = set ? rkl : rk;
+      const rsrc_t& rvs = set ? rvl : rv;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int b = wave + NW * i;
+        if (i < 2)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (lds_ptr_t)(base + i * KT + wave * 8 * BK), 16, voff[i],
+                                                   key0 * kAttnD * 2u, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs, (lds_ptr_t)(base + 2 * KT + (b - 16) * 8 * BK), 16, voff[i],
+                                                   key0 * 2u, 0, 0);
+      }
     }
   };
 
@@ -162,16 +194,18 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
     }
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      u32x4 a[4];
+      u32x4 a[4], al[4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) a[kt] = lds_read16(st + (d >> 1) * KT, fo.off[d & 1] + kt * 16 * BK);
+      for (int kt = 0; kt < 4; ++kt) {
+        a[kt] = lds_read16(st + (d >> 1) * KT, fo.off[d & 1] + kt * 16 * BK);
+        if constexpr (SKV) al[kt] = lds_read16(st + HALF + (d >> 1) * KT, fo.off[d & 1] + kt * 16 * BK);
+      }
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         sh[kt] = mfma<0, MFL_F16>(a[kt], qh[d], sh[kt]);
-        if constexpr (CHAINS == 2)
-          sl[kt] = mfma<0, MFL_F16>(a[kt], ql[d], sl[kt]);
-        else
-          sh[kt] = mfma<0, MFL_F16>(a[kt], ql[d], sh[kt]);
+        f32x4& corr = CHAINS == 2 ? sl[kt] : sh[kt];
+        corr = mfma<0, MFL_F16>(a[kt], ql[d], corr);
+        if constexpr (SKV) corr = mfma<0, MFL_F16>(al[kt], qh[d], corr);
       }
     }
   };
@@ -238,10 +272,9 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
       for (int i = 0; i < 8; ++i) {
         const u32x4 a = lds_read16(sv, fo.off[t] + i * 16 * BK);
         oh[i] = mfma<0, MFL_F16>(a, ph[t], oh[i]);
-        if constexpr (CHAINS == 2)
-          ol[i] = mfma<0, MFL_F16>(a, pl[t], ol[i]);
-        else
-          oh[i] = mfma<0, MFL_F16>(a, pl[t], oh[i]);
+        f32x4& corr = CHAINS == 2 ? ol[i] : oh[i];
+        corr = mfma<0, MFL_F16>(a, pl[t], corr);
+        if constexpr (SKV) corr = mfma<0, MFL_F16>(lds_read16(sv + HALF, fo.off[t] + i * 16 * BK), ph[t], corr);
       }
   };
 
@@ -327,14 +360,14 @@ int64_t attn_fused_splits(int64_t nq, int64_t nk) {
   return s;
 }
 
-int64_t attn_fused_workspace(int64_t nq, int64_t nk) {
+int64_t attn_fused_workspace(int64_t nq, int64_t nk, bool skv) {
   auto al = [](int64_t x) { return (x + 255) & ~(int64_t)255; };
   const int64_t s = attn_fused_splits(nq, nk);
-  return al(nk * kAttnD * 2) * 2 + al(s * nq * kAttnD * 4) + 2 * al(s * nq * 4);
+  return al(nk * kAttnD * 2) * (skv ? 4 : 2) + al(s * nq * kAttnD * 4) + 2 * al(s * nq * 4);
 }
 
-int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, const float* v, int chains, float* o,
-                      void* workspace, hipStream_t st) {
+int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, const float* v, int chains, bool skv,
+                      float* o, void* workspace, hipStream_t st) {
   auto al = [](int64_t x) { return (x + 255) & ~(int64_t)255; };
   const int64_t splits = attn_fused_splits(nq, nk);
   char* w = (char*)workspace;
@@ -342,12 +375,24 @@ int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, co
   w += al(nk * kAttnD * 2);
   uint16_t* vt = (uint16_t*)w;
   w += al(nk * kAttnD * 2);
+  uint16_t* kl = nullptr;
+  uint16_t* vtl = nullptr;
+  if (skv) {
+    kl = (uint16_t*)w;
+    w += al(nk * kAttnD * 2);
+    vtl = (uint16_t*)w;
+    w += al(nk * kAttnD * 2);
+  }
   float* op = (float*)w;
   w += al(splits * nq * kAttnD * 4);
   float* mp = (float*)w;
   w += al(splits * nq * 4);
   float* lp = (float*)w;
-  hipLaunchKernelGGL(attn_prep, dim3((unsigned)(nk / 32)), dim3(256), 0, st, k, v, kq, vt, (int)nk);
+  const dim3 pgrid((unsigned)(nk / 32)), pblock(256);
+  if (skv)
+    hipLaunchKernelGGL(attn_prep<true>, pgrid, pblock, 0, st, k, v, kq, vt, kl, vtl, (int)nk);
+  else
+    hipLaunchKernelGGL(attn_prep<false>, pgrid, pblock, 0, st, k, v, kq, vt, kl, vtl, (int)nk);
   const int qblocks = (int)(nq / kAttnQ);
   const int nwg = qblocks * (int)splits;
   const int xcd_map = nwg % 8 == 0;
@@ -355,12 +400,21 @@ int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, co
   const dim3 grid((unsigned)nwg), block(512);
   // two LDS stages: measured as fast as three, and a third adds nothing at
   // one workgroup per CU
-  if (chains == 2)
-    hipLaunchKernelGGL((attn_fused_kernel<2, 2>), grid, block, 0, st, q, kq, vt, op, mp, lp, (int)nq, (int)nk, kps,
-                       qblocks, xcd_map);
-  else
-    hipLaunchKernelGGL((attn_fused_kernel<1, 2>), grid, block, 0, st, q, kq, vt, op, mp, lp, (int)nq, (int)nk, kps,
-                       qblocks, xcd_map);
+#define MFL_ATTN_LAUNCH(CH, SK)                                                                                      \
+  hipLaunchKernelGGL((attn_fused_kernel<CH, 2, SK>), grid, block, 0, st, q, kq, vt, kl, vtl, op, mp, lp, (int)nq,      \
+                     (int)nk, kps, qblocks, xcd_map)
+  if (skv) {
+    if (chains == 2)
+      MFL_ATTN_LAUNCH(2, true);
+    else
+      MFL_ATTN_LAUNCH(1, true);
+  } else {
+    if (chains == 2)
+      MFL_ATTN_LAUNCH(2, false);
+    else
+      MFL_ATTN_LAUNCH(1, false);
+  }
+#undef MFL_ATTN_LAUNCH
   const int64_t vec = nq * kAttnD / 4;
   const dim3 cgrid((unsigned)((vec + 255) / 256)), cblock(256);
   switch (splits) {

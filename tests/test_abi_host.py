@@ -276,7 +276,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-null value; never dereferenced (rejected
     (lambda m: m.attention_split_fp32(2048, 32768, 64, FAKE, FAKE, FAKE, 2, 1, FAKE, FAKE, 1 << 40), -3),
     (lambda m: m.attention_split_fp32(2000, 32768, 128, FAKE, FAKE, FAKE, 2, 0, FAKE, FAKE, 1 << 40), -3),
     (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 3, 1, FAKE, FAKE, 1 << 40), -1),
-    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 2, FAKE, FAKE, 1 << 40), -1),
+    (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 3, FAKE, FAKE, 1 << 40), -1),
     (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 0, FAKE, FAKE, 1024), -1),
     (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 1, FAKE, FAKE, 1024), -1),
     (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 1, FAKE, FAKE + 16, 1 << 40), -1),
@@ -347,8 +347,12 @@ def test_attention_workspace_size(lib):
     assert 2 * 32768 * 128 * 2 < f < b // 4
     with pytest.raises(lib.MflError):
         lib.attention_workspace_bytes(2048, 32768, 96, 1)
+    skv = lib.attention_workspace_bytes(2048, 32768, 128, 2)
+    assert skv == f + 2 * 32768 * 128 * 2      # K and V^T lo planes on top
     with pytest.raises(lib.MflError):
         lib.attention_workspace_bytes(2048, 32768, 128, 5)
+    with pytest.raises(lib.MflError):
+        lib.attention_workspace_bytes(2048, 32768, 128, 3)
 
 
 def test_plain_c_program_uses_the_header_and_library(tmp_path):

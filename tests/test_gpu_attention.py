@@ -75,3 +75,41 @@ def test_attention_full_size_sampled():
     print("attention full-size errors (algo, chains):", errs)
     assert errs[(mfl.ATTN_MATERIALISED, 2)] <= 5e-6
     assert errs[(mfl.ATTN_FUSED, 2)] <= 5e-6
+
+
+# ---- algo 2: K and V split as well; reference on the original fp32 K and V
+
+@pytest.mark.parametrize("chains", [1, 2])
+@pytest.mark.parametrize("nq,nk", [(128, 128), (128, 384), (256, 640), (384, 4096)])
+def test_attention_split_kv_small(nq, nk, chains):
+    q, k, v = inputs.attention(nq, nk)
+    say("attention split kv", nq, nk, chains)
+    o = run_attention(q, k, v, chains, mfl.ATTN_FUSED_SPLIT_KV)
+    err = R.rel_error(o, R.attention_ref(q, k, v, round_kv=False))
+    print(f"attention split-kv {nq}x{nk} chains={chains} err={err:.3e}")
+    assert err <= 5e-6
+
+
+def test_attention_split_kv_large_scores():
+    q, k, v = inputs.attention(256, 4096)
+    q = (q * 100.0).astype(np.float32)
+    say("attention split kv large scores")
+    o = run_attention(q, k, v, 2, mfl.ATTN_FUSED_SPLIT_KV)
+    assert R.rel_error(o, R.attention_ref(q, k, v, round_kv=False)) <= 5e-6
+
+
+def test_attention_split_kv_full_size_removes_the_rounding_floor():
+    """2048 x 32768: against the reference on the ORIGINAL K and V, rounding K
+    and V once (algo 1) leaves an error floor; splitting them (algo 2) removes it."""
+    q, k, v = inputs.attention()
+    rows = np.random.default_rng(16).choice(2048, 64, replace=False)
+    ref = R.attention_ref(q[rows], k, v, round_kv=False)
+    errs = {}
+    for algo in (mfl.ATTN_FUSED, mfl.ATTN_FUSED_SPLIT_KV):
+        say("attention vs fp32 K/V reference", algo)
+        o = run_attention(q, k, v, 2, algo)
+        assert not np.isnan(o).any()
+        errs[algo] = R.rel_error(o[rows], ref)
+    print("errors against the fp32-K/V reference (algo 1, algo 2):", errs)
+    assert errs[mfl.ATTN_FUSED_SPLIT_KV] <= 5e-6
+    assert errs[mfl.ATTN_FUSED] >= 10 * errs[mfl.ATTN_FUSED_SPLIT_KV]
