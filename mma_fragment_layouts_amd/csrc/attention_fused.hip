@@ -71,6 +71,21 @@ __global__ __launch_bounds__(256) void attn_prep(const float* __restrict__ K, co
   }
 }
 
+// Maximum over lanes l, l^16, l^32, l^48 without a round trip through the LDS:
+// v_permlane16_swap (v_permlane32_swap) with the same value in both operands
+// hands every lane the pair {x[l & ~16], x[l | 16]} ({x[l & ~32], x[l | 32]}),
+// as a one-wave probe of the instructions shows.  The two results are copied
+// to scalars before the bit cast: a bit cast taken straight from an element of
+// the returned pair reads element 0 for both (and the max then vanishes).
+__device__ __forceinline__ float swap_max(float x, bool by32) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  const auto r = by32 ? __builtin_amdgcn_permlane32_swap(b, b, false, false)
+                      : __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+__device__ __forceinline__ float max_over_lane_groups(float x) { return swap_max(swap_max(x, false), true); }
+
 // Workgroup -> (query block, key slice).  With xcd_map the workgroups that an
 // XCD receives (hardware dispatch sends workgroup b to XCD b mod 8) cover a
 // contiguous range of key slices for every query block, so each XCD's L2 holds
@@ -230,8 +245,7 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
 #pragma unroll
       for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, sh[kt][j]);
     }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    cmax = max_over_lane_groups(cmax);
     if (__builtin_amdgcn_ballot_w64(cmax > mref + kAttnSlack) != 0) {
       const float mnew = fmaxf(mref, cmax);
       const float sc = __builtin_amdgcn_exp2f(mref - mnew);  // 0 on the first chunk (mref = -inf)
