@@ -275,3 +275,29 @@ def test_mma_through_library_layouts_matches_host_matmul(shape, orders, fmt):
     want = np.full(ch.shape, -3.0)
     want[row0:row0 + mn, col0:col0 + mn] = exact
     assert np.array_equal(ch, want)
+
+
+@pytest.mark.parametrize("fmt,val,scale", [("f16", 2.0 ** -20, 1.0), ("f16", 2.0 ** -24, 1.0),
+                                           ("bf16", 2.0 ** -130, 2.0 ** 10), ("bf16", 2.0 ** -133, 2.0 ** 12)])
+@pytest.mark.parametrize("shape", [0, 1])
+def test_mfma_subnormal_inputs(shape, fmt, val, scale):
+    """Subnormal 16-bit operands enter the product unflushed: the lo halves of
+    the split (about 2^-11 of a value, so subnormal for small fp16 values) rely
+    on it.  Products are chosen to be normal fp32 numbers, compared exactly."""
+    fm, mn, k = GEOM[shape]
+    a = np.zeros((mn, k), np.float32)
+    b = np.zeros((k, mn), np.float32)
+    a[3, 5], b[5, 7] = val, scale            # C[3][7] = val * scale
+    a[4, 6], b[6, 7] = 3 * val, scale        # C[4][7] = 3 val * scale (3 val still subnormal)
+    a[9, 1], a[9, 2], b[1, 2], b[2, 2] = val, val, scale, scale   # C[9][2] = 2 val * scale (a sum)
+    from oracle import formats as OF
+    assert OF.quantize(np.float32(val), fmt) == val and OF.quantize(np.float32(3 * val), fmt) == 3 * val
+    say("mfma subnormal inputs", shape, fmt, val)
+    acc = run_probe(shape, fmt, a, b)
+    got = np.zeros((mn, mn))
+    for l in range(64):
+        for j in range(fm.per_lane):
+            got[fm.coords(l, j)] = acc[l, j]
+    want = np.zeros((mn, mn))
+    want[3, 7], want[4, 7], want[9, 2] = val * scale, 3 * val * scale, 2 * val * scale
+    assert np.array_equal(got, want), (got[3, 7], got[4, 7], got[9, 2])
