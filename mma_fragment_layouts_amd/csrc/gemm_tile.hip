@@ -207,11 +207,27 @@ template <int DT>
 static int dispatch(int shape, const void* a, int64_t lda, int oa, const void* b, int64_t ldb, int ob, float* c,
                     int64_t ldc, int M, int N, int K, int accumulate, hipStream_t s) {
   const bool ak = oa == MFL_ROW_MAJOR, bk = ob == MFL_COL_MAJOR;
-  if (ak && bk && M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && fast_fits(lda, ldb, ldc)) {
-    // 16 waves (4 per SIMD), 64 x 64 outputs per wave
-    if (shape == MFL_MFMA_32X32X16)
-      return launch_fast<256, 256, 4, 4, 1, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-    return launch_fast<256, 256, 4, 4, 0, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  if (ak && bk && K % 64 == 0 && fast_fits(lda, ldb, ldc)) {
+    // The largest tile that still gives the chip at least 128 workgroups:
+    // 256 x 256 (16 waves of 64 x 64), 128 x 128 (4 waves of 64 x 64), or for
+    // small problems 64 x 64 (2 waves of 32 x 64), where a single big tile would
+    // leave all but a few CUs idle.
+    const auto count = [&](int t) { return (int64_t)(M / t) * (N / t); };
+    if (M % 256 == 0 && N % 256 == 0 && count(256) >= 128) {
+      if (shape == MFL_MFMA_32X32X16)
+        return launch_fast<256, 256, 4, 4, 1, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+      return launch_fast<256, 256, 4, 4, 0, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+    }
+    if (M % 128 == 0 && N % 128 == 0 && count(128) >= 128) {
+      if (shape == MFL_MFMA_32X32X16)
+        return launch_fast<128, 128, 2, 2, 1, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+      return launch_fast<128, 128, 2, 2, 0, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+    }
+    if (M % 64 == 0 && N % 64 == 0) {
+      if (shape == MFL_MFMA_32X32X16)
+        return launch_fast<64, 64, 2, 1, 1, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+      return launch_fast<64, 64, 2, 1, 0, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+    }
   }
   if (ak && bk) return launch_generic<DT, true, true>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
   if (ak) return launch_generic<DT, true, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);

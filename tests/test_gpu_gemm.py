@@ -159,3 +159,27 @@ def test_dense_4096_bf16_sampled(shape):
     # elementwise: fp32 accumulation of 4096 products, bound ~ K * u32 * sum|a||b|
     scale = np.abs(ref).max()
     assert np.max(np.abs(ch[r, cc] - ref)) <= 4096 * 2.0 ** -24 * 64 * max(scale, 1.0)
+
+
+# The fast path picks its tile by problem size: 64 x 64 (2 waves) for small
+# problems, 128 x 128 (4 waves) in between, 256 x 256 (16 waves) from 128 such
+# tiles up.  Each size below lands on one of them (comment), with both MFMA
+# instructions and both 16-bit types; accumulate on for one of each.
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [0, 1])
+@pytest.mark.parametrize("mnk,accumulate", [((256, 256, 256), 0),     # 64 x 64, 16 workgroups
+                                             ((192, 320, 128), 1),     # 64 x 64 (not a multiple of 128)
+                                             ((1024, 1024, 512), 0),   # 64 x 64, 256 workgroups
+                                             ((2048, 2048, 256), 1),   # 128 x 128, 256 workgroups
+                                             ((2048, 4096, 128), 0)])  # 256 x 256, 128 workgroups
+def test_fast_path_tile_sizes(mnk, accumulate, shape, fmt):
+    m, n, k = mnk
+    rng = np.random.default_rng(m + n + k + shape)
+    a = rng.uniform(-1, 1, (m, k)).astype(np.float32)
+    bt = rng.uniform(-1, 1, (n, k)).astype(np.float32)
+    c0 = rng.standard_normal((m, n)).astype(np.float32) if accumulate else None
+    say("gemm fast tiles", m, n, k, shape, fmt, accumulate)
+    c = run_gemm(fmt, a, bt.T, shape=shape, accumulate=accumulate, c0=c0)
+    ref = R.gemm_ref(a, bt, fmt) + (c0.astype(np.float64) if accumulate else 0.0)
+    assert not np.isnan(c).any()
+    assert R.rel_error(c, ref) <= TOL
