@@ -170,6 +170,10 @@ bool valid_sizes(int64_t nq, int64_t nk, int64_t d) {
          nq * nk <= ((int64_t)1 << 34);
 }
 
+// The fused kernel addresses K16 and V16^T through buffer descriptors with a
+// 32-bit byte extent (nk * 128 * 2 bytes).
+bool fused_fits(int64_t nk) { return nk * kAttnD * 2 <= (int64_t)UINT32_MAX; }
+
 }  // namespace
 }  // namespace mfl
 
@@ -177,7 +181,7 @@ using namespace mfl;
 
 extern "C" int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int algo, int64_t* bytes) {
   if (!bytes || algo < 0 || algo > 2) return MFL_EINVAL;
-  if (!valid_sizes(nq, nk, d)) return MFL_EUNSUPPORTED;
+  if (!valid_sizes(nq, nk, d) || (algo >= 1 && !fused_fits(nk))) return MFL_EUNSUPPORTED;
   *bytes = algo == 0 ? plan(nq, nk, d).total : attn_fused_workspace(nq, nk, algo == 2);
   return MFL_OK;
 }
@@ -193,6 +197,7 @@ extern "C" int attention_split_fp32(int64_t nq, int64_t nk, int64_t d, const flo
   if (((uintptr_t)workspace & 255) != 0) return MFL_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   if (algo >= 1) {
+    if (!fused_fits(nk)) return MFL_EUNSUPPORTED;
     const bool skv = algo == 2;
     if (workspace_bytes < attn_fused_workspace(nq, nk, skv)) return MFL_EINVAL;
     return launch_attn_fused(nq, nk, q, k, v, chains, skv, o, workspace, s);

@@ -277,6 +277,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-null value; never dereferenced (rejected
     (lambda m: m.attention_split_fp32(2000, 32768, 128, FAKE, FAKE, FAKE, 2, 0, FAKE, FAKE, 1 << 40), -3),
     (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 3, 1, FAKE, FAKE, 1 << 40), -1),
     (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 3, FAKE, FAKE, 1 << 40), -1),
+    (lambda m: m.attention_split_fp32(128, 1 << 24, 128, FAKE, FAKE, FAKE, 2, 1, FAKE, FAKE, 1 << 40), -3),
     (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 0, FAKE, FAKE, 1024), -1),
     (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 1, FAKE, FAKE, 1024), -1),
     (lambda m: m.attention_split_fp32(2048, 32768, 128, FAKE, FAKE, FAKE, 2, 1, FAKE, FAKE + 16, 1 << 40), -1),
@@ -347,6 +348,13 @@ def test_attention_workspace_size(lib):
     assert 2 * 32768 * 128 * 2 < f < b // 4
     with pytest.raises(lib.MflError):
         lib.attention_workspace_bytes(2048, 32768, 96, 1)
+    # the fused kernel's 32-bit buffer extent: nk * 128 * 2 bytes must fit
+    assert lib.attention_workspace_bytes(128, (1 << 24) - 128, 128, 1) > 0
+    for algo in (1, 2):
+        with pytest.raises(lib.MflError) as e:
+            lib.attention_workspace_bytes(128, 1 << 24, 128, algo)
+        assert e.value.status == lib.EUNSUPPORTED
+    assert lib.attention_workspace_bytes(128, 1 << 24, 128, 0) > 0
     skv = lib.attention_workspace_bytes(2048, 32768, 128, 2)
     assert skv == f + 2 * 32768 * 128 * 2      # K and V^T lo planes on top
     with pytest.raises(lib.MflError):
