@@ -293,7 +293,9 @@ MFL_API int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int alg
  *           then has the three terms hi*hi, hi*lo, lo*hi; with chains = 2 the
  *           two corrections share the second chain), so every operand enters
  *           at fp32-input accuracy instead of K and V being rounded once.
- * Supported: d = 128, nq and nk multiples of 128.  `workspace` is device memory
+ * Supported: d = 128, nq and nk multiples of 128, and for algo 1 and 2
+ * nk < 2^24 (the fused kernel's 32-bit buffer extent); others return
+ * MFL_EUNSUPPORTED.  `workspace` is device memory
  * of at least attention_workspace_bytes(..., algo) bytes, 256-byte aligned. */
 MFL_API int attention_split_fp32(int64_t nq, int64_t nk, int64_t d, const float *q, const float *k,
                                  const float *v, int chains, int algo, float *o, void *workspace,
