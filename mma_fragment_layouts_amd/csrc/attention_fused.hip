@@ -26,9 +26,11 @@ __device__ __forceinline__ Split2 split2(float a, float b) {
 // One workgroup per 32-key block (256 threads):
 //   K (nk x 128 fp32) -> K16 (nk x 128 fp16, round to nearest even);
 //   V (nk x 128 fp32) -> V16^T (128 x nk fp16), the keys of each 32-key block
-//   stored at vt_key_pos(r).  Thread (dim, half) gathers the 16 keys of
-//   storage positions 16 half .. 16 half + 15 for one dim: a wave's 64 lanes
-//   read 64 consecutive dims of one key per load.
+//   stored at vt_key_pos(r).
+// K: thread t converts 16 consecutive values (four 16-byte loads, two 16-byte
+// stores).  V: thread (pair, oct) gathers dims 2 pair, 2 pair + 1 of the keys
+// at storage positions 8 oct .. 8 oct + 7 (8-byte loads: a wave's 64 lanes read
+// one whole 512-byte key row per load) and stores 16 bytes per dim.
 // SKV: K and V are split as well — K16 and V16^T hold the hi parts and Kl and
 // Vtl (same layouts) the lo parts, lo = RNE16(x - hi).
 template <bool SKV>
@@ -37,37 +39,54 @@ __global__ __launch_bounds__(256) void attn_prep(const float* __restrict__ K, co
                                                  uint16_t* __restrict__ Kl, uint16_t* __restrict__ Vtl, int nk) {
   const int blk = blockIdx.x, t = threadIdx.x;
   const int64_t base = (int64_t)blk * 32 * kAttnD;
+  {
+    const int64_t idx = base + (int64_t)t * 16;
+    uint32_t wh[8], wl[8];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int idx = (r * 256 + t) * 4;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(K + base + idx);
-    const Split2 a = split2(x[0], x[1]), b = split2(x[2], x[3]);
-    const uint32_t wh[2] = {a.hi, b.hi};
-    __builtin_memcpy(Kq + base + idx, wh, 8);
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(K + idx + 4 * q);
+      const Split2 a = split2(x[0], x[1]), b = split2(x[2], x[3]);
+      wh[2 * q] = a.hi;
+      wh[2 * q + 1] = b.hi;
+      wl[2 * q] = a.lo;
+      wl[2 * q + 1] = b.lo;
+    }
+    u32x4 o;
+    __builtin_memcpy(&o, wh, 16);
+    *reinterpret_cast<u32x4*>(Kq + idx) = o;
+    __builtin_memcpy(&o, wh + 4, 16);
+    *reinterpret_cast<u32x4*>(Kq + idx + 8) = o;
     if constexpr (SKV) {
-      const uint32_t wl[2] = {a.lo, b.lo};
-      __builtin_memcpy(Kl + base + idx, wl, 8);
+      __builtin_memcpy(&o, wl, 16);
+      *reinterpret_cast<u32x4*>(Kl + idx) = o;
+      __builtin_memcpy(&o, wl + 4, 16);
+      *reinterpret_cast<u32x4*>(Kl + idx + 8) = o;
     }
   }
-  const int dim = t & (kAttnD - 1), half = t >> 7;
-  uint16_t h[16], l[16];
+  const int pair = t & 63, oct = t >> 6;  // dims 2 pair, 2 pair + 1; positions 8 oct ..
+  uint16_t h0[8], h1[8], l0[8], l1[8];
 #pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    const float x = V[base + (int64_t)vt_pos_key(16 * half + p) * kAttnD + dim];
-    h[p] = to16<MFL_F16>(x);
-    if constexpr (SKV) l[p] = to16<MFL_F16>(x - from16<MFL_F16>(h[p]));
+  for (int p = 0; p < 8; ++p) {
+    const f32x2 x =
+        *reinterpret_cast<const f32x2*>(V + base + (int64_t)vt_pos_key(8 * oct + p) * kAttnD + 2 * pair);
+    h0[p] = to16<MFL_F16>(x.x);
+    h1[p] = to16<MFL_F16>(x.y);
+    if constexpr (SKV) {
+      l0[p] = to16<MFL_F16>(x.x - from16<MFL_F16>(h0[p]));
+      l1[p] = to16<MFL_F16>(x.y - from16<MFL_F16>(h1[p]));
+    }
   }
-  const int64_t doff = (int64_t)dim * nk + (int64_t)blk * 32 + 16 * half;
-  u32x4 o0, o1;
-  __builtin_memcpy(&o0, h, 16);
-  __builtin_memcpy(&o1, h + 8, 16);
-  *reinterpret_cast<u32x4*>(Vt + doff) = o0;
-  *reinterpret_cast<u32x4*>(Vt + doff + 8) = o1;
+  const int64_t d0 = (int64_t)(2 * pair) * nk + (int64_t)blk * 32 + 8 * oct;
+  u32x4 o;
+  __builtin_memcpy(&o, h0, 16);
+  *reinterpret_cast<u32x4*>(Vt + d0) = o;
+  __builtin_memcpy(&o, h1, 16);
+  *reinterpret_cast<u32x4*>(Vt + d0 + nk) = o;
   if constexpr (SKV) {
-    __builtin_memcpy(&o0, l, 16);
-    __builtin_memcpy(&o1, l + 8, 16);
-    *reinterpret_cast<u32x4*>(Vtl + doff) = o0;
-    *reinterpret_cast<u32x4*>(Vtl + doff + 8) = o1;
+    __builtin_memcpy(&o, l0, 16);
+    *reinterpret_cast<u32x4*>(Vtl + d0) = o;
+    __builtin_memcpy(&o, l1, 16);
+    *reinterpret_cast<u32x4*>(Vtl + d0 + nk) = o;
   }
 }
 
