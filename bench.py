@@ -145,7 +145,7 @@ def sclk_under_load(step, torch, seconds=1.0):
     return found.get("mhz")
 
 
-EXTRA = ("gemm_256", "block_repeat", "split", "attention")
+EXTRA = ("gemm_256", "gemm_orders", "block_repeat", "split", "attention")
 
 
 def extra_workloads(torch, mfl, inputs, stream, which=EXTRA):
@@ -160,6 +160,8 @@ def extra_workloads(torch, mfl, inputs, stream, which=EXTRA):
 
     if "gemm_256" in which:
         gemm_256(torch, mfl, inputs, stream, dev, q16, out)
+    if "gemm_orders" in which:
+        gemm_orders(torch, mfl, inputs, stream, dev, q16, out)
     if "block_repeat" in which:
         block_repeat(torch, mfl, inputs, stream, dev, q16, out)
     if "split" in which:
@@ -179,6 +181,35 @@ def gemm_256(torch, mfl, inputs, stream, dev, q16, out):
                            "bound": "latency (16 workgroups)",
                            "frac_mfma_peak": round(2 * 256 ** 3 / ms / 1e9 / PEAK_BF16_TFLOPS, 5)}
 
+
+
+def gemm_orders(torch, mfl, inputs, stream, dev, q16, out):
+    """The 4096^3 bf16 GEMM in each operand order (ld 4160, NaN padding).  A
+    column-major or B row-major operand is staged as k-major LDS slabs and read
+    with the transpose read."""
+    a, bt = inputs.gemm_dense()
+    n = 4096
+
+    def padded(x):
+        s = np.full((n, 4160), np.nan, np.float32)
+        s[:, :n] = x
+        return s
+
+    store_a = {mfl.ROW_MAJOR: a, mfl.COL_MAJOR: padded(a[:, :n].T)}
+    store_b = {mfl.COL_MAJOR: bt, mfl.ROW_MAJOR: padded(bt[:, :n].T)}
+    name = {mfl.ROW_MAJOR: "row", mfl.COL_MAJOR: "col"}
+    c = torch.empty((n, n), device=dev)
+    res = {}
+    for oa in (mfl.ROW_MAJOR, mfl.COL_MAJOR):
+        for ob in (mfl.COL_MAJOR, mfl.ROW_MAJOR):
+            da, db = q16(store_a[oa], mfl.BF16), q16(store_b[ob], mfl.BF16)
+            ms = best_of(lambda: mfl.gemm_tile_mma(mfl.BF16, n, n, n, da, 4160, oa, db, 4160, ob, c, n, 0, stream),
+                         stream)
+            tf = 2 * n ** 3 / ms / 1e9
+            res[f"A_{name[oa]}_B_{name[ob]}"] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                                                 "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            del da, db
+    out["gemm_4096_bf16_orders"] = res
 
 
 def block_repeat(torch, mfl, inputs, stream, dev, q16, out):

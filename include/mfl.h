@@ -191,8 +191,13 @@ MFL_API int split_fp32(int dtype, const float *x, void *hi, void *lo, int64_t n,
  * (accumulate = 1) with `dtype` operands (MFL_F16 or MFL_BF16) and fp32
  * accumulation kept in registers across the whole K loop; each output tile is
  * stored once through the accumulator layout (Warp issue #1965, "Proposed
- * change" and "Design consequences").  Operand orders are free; the fast path
- * is row-major A with column-major B (both K-contiguous). */
+ * change" and "Design consequences").  Operand orders are free.  The fast path
+ * takes M and N multiples of 128 (of 64 when A is row-major and B
+ * column-major), K a multiple of 64, and buffers within 4 GiB (256 rows of
+ * lda / ldb / ldc; K rows of lda for column-major A, of ldb for row-major B);
+ * a column-major A or row-major B is staged K-major in LDS and read with the
+ * gfx950 transpose read, with results bit-identical to the K-contiguous
+ * orders.  Other sizes take the generic path. */
 MFL_API int gemm_tile_mma(int dtype, int64_t m, int64_t n, int64_t k,
                   const void *a, int64_t lda, int order_a,
                   const void *b, int64_t ldb, int order_b,
@@ -267,7 +272,7 @@ MFL_API int gemm_split_fp32_ws(int piece, int64_t m, int64_t n, int64_t k,
 
 /* gemm_tile_mma with an explicit MFMA instruction for the fast path
  * (MFL_MFMA_16X16X32 or MFL_MFMA_32X32X16); gemm_tile_mma uses 16x16x32.  The
- * generic path (other orders, ragged sizes) always uses 16x16x32. */
+ * generic path (ragged sizes) always uses 16x16x32. */
 MFL_API int gemm_tile_mma_shape(int shape, int dtype, int64_t m, int64_t n, int64_t k,
                                 const void *a, int64_t lda, int order_a,
                                 const void *b, int64_t ldb, int order_b,

@@ -108,6 +108,71 @@ __device__ __forceinline__ int lds_elem(int row, int k) {
   return lds_chunk<BK>(row, k >> 3) + (k & 7);
 }
 
+// ---- k-major LDS tiles and the CDNA4 transpose read ---------------------------
+// A K-strided operand (A column-major, B row-major) is staged as a k-major tile:
+// 64 K rows of R consecutive M (or N) values (R = 128 or 256).
+//
+// ds_read_b64_tr_b16 (gfx950) reads 8 bytes per lane and transposes 16-bit
+// elements inside each group of 16 lanes: lane 16g + 4q + e receives, as its
+// element t, element e of the 8 bytes that lane 16g + 4t + q addressed (q, e, t
+// in 0..3).  Measured on MI355X by reading an index-filled LDS under several
+// address patterns; the mapping does not depend on the addresses.
+MFL_HD constexpr int tr_src_lane(int lane, int t) { return (lane & ~15) + 4 * t + ((lane & 15) >> 2); }
+MFL_HD constexpr int tr_src_elem(int lane) { return lane & 3; }
+
+// Layout of the k-major tile: element (k, r) at 16-bit offset
+// 8 * kmaj_chunk(k, r) + (r & 7), the 16-byte chunk index being a permutation of
+// the bits of k and r.  ds_read_b64 and ds_read_b64_tr_b16 serve a wave in two
+// phases, lanes 0-31 and 32-63 (measured with SQ_LDS_BANK_CONFLICT on lane
+// pairs); a fragment read touches, per phase, 8 K rows x 32 bytes (16x16x32:
+// k bits 0, 1, 3 and r bit 3 vary) or 4 K rows x 64 bytes (32x32x16: k bits 0,
+// 1 and r bits 3, 4 vary).  Those bits become chunk bits 0-3 — the 16 bank slots
+// of 256 bytes — so every phase is conflict free.  The bits that step a read
+// (the second read of a fragment: k bit 2; the MFMA K step: k bit 5, or bits 4
+// and 5; the fragment: r bits 4-5, or bit 5) sit above them, so every read is an
+// immediate offset from one per-lane address.  A direct-to-LDS load
+// instruction fills 64 consecutive chunks: its lanes fetch 8 K rows x 128
+// contiguous bytes, and instruction and wave indices map to fixed (k, r)
+// offsets — uniform scalar offsets.
+template <int SHAPE>
+MFL_HD constexpr int kmaj_chunk(int k, int r) {
+  const int k0 = k & 1, k1 = (k >> 1) & 1, k2 = (k >> 2) & 1, k3 = (k >> 3) & 1, k4 = (k >> 4) & 1, k5 = (k >> 5) & 1;
+  const int r3 = (r >> 3) & 1, r4 = (r >> 4) & 1, r5 = (r >> 5) & 1, rh = r >> 6;
+  if (SHAPE == 0)
+    return r3 | k0 << 1 | k1 << 2 | k3 << 3 | r4 << 4 | r5 << 5 | k2 << 6 | k4 << 7 | k5 << 8 | rh << 9;
+  return r3 | k0 << 1 | k1 << 2 | r4 << 3 | r5 << 4 | k3 << 5 | k2 << 6 | k4 << 7 | k5 << 8 | rh << 9;
+}
+// Inverse of kmaj_chunk: the (k, r) of the first element of chunk c.
+template <int SHAPE>
+MFL_HD constexpr void kmaj_coords(int c, int* k, int* r) {
+  auto bit = [c](int i) { return (c >> i) & 1; };
+  if (SHAPE == 0) {
+    *k = bit(1) | bit(2) << 1 | bit(6) << 2 | bit(3) << 3 | bit(7) << 4 | bit(8) << 5;
+    *r = (bit(0) << 3) | (bit(4) << 4) | (bit(5) << 5) | ((c >> 9) << 6);
+  } else {
+    *k = bit(1) | bit(2) << 1 | bit(6) << 2 | bit(5) << 3 | bit(7) << 4 | bit(8) << 5;
+    *r = (bit(0) << 3) | (bit(3) << 4) | (bit(4) << 5) | ((c >> 9) << 6);
+  }
+}
+template <int SHAPE>
+MFL_HD constexpr int lds_elemKM(int k, int r) {
+  return 8 * kmaj_chunk<SHAPE>(k, r) + (r & 7);
+}
+template <int SHAPE, int R>
+constexpr bool kmaj_layout_ok() {
+  for (int k = 0; k < 64; ++k)
+    for (int r = 0; r < R; r += 8) {
+      const int c = kmaj_chunk<SHAPE>(k, r);
+      int k2 = -1, r2 = -1;
+      kmaj_coords<SHAPE>(c, &k2, &r2);
+      if (c < 0 || c >= 8 * R || k2 != k || r2 != r) return false;
+    }
+  return true;
+}
+static_assert(kmaj_layout_ok<0, 128>() && kmaj_layout_ok<0, 256>() && kmaj_layout_ok<1, 128>() &&
+                  kmaj_layout_ok<1, 256>(),
+              "k-major tile layout must be a bijection with the stated inverse");
+
 // ---- buffer resources --------------------------------------------------------
 // A raw buffer descriptor: base address, byte extent (accesses at or past it
 // read 0 / are dropped), 32-bit dword format.  Per-lane 32-bit offsets plus
@@ -123,6 +188,16 @@ __device__ __forceinline__ u32x4 lds_read16(const uint16_t* lds, int elem_off) {
 }
 __device__ __forceinline__ void lds_write16(uint16_t* lds, int elem_off, u32x4 v) {
   *reinterpret_cast<u32x4*>(lds + elem_off) = v;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// Two transpose reads, `step` elements apart, concatenated into one 8-element
+// MFMA operand (elements 0-3 from the first read, 4-7 from the second).
+__device__ __forceinline__ u32x4 lds_read_tr(const uint16_t* lds, int elem_off, int step) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + elem_off));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + elem_off + step));
+  return __builtin_shufflevector(__builtin_bit_cast(u32x2, lo), __builtin_bit_cast(u32x2, hi), 0, 1, 2, 3);
 }
 
 __device__ __forceinline__ u32x4 gload16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }

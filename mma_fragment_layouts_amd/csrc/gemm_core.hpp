@@ -105,20 +105,108 @@ struct FragOffsets {
   }
 };
 
+// Fragment reads from a k-major tile (K-strided operands) with two transpose
+// reads.  Lane l of the 16-lane group g addresses K row kb(g) + ((l >> 2) & 3)
+// + 4h and columns rb(g) + 4*(l & 3) .. +3 in read h = 0, 1, where
+// kb(g) = 8*(16g div MN) and rb(g) = 16g mod MN; after the transpose lane l holds
+// row (l mod MN) at K positions 8*(l div MN) + 4h .. +3, i.e. elements 4h .. 4h+3
+// of the instruction's operand numeral (checked below).
+template <int SHAPE>
+MFL_HD constexpr int tr_k(int lane) {
+  return 8 * ((16 * (lane >> 4)) / Shape<SHAPE>::MN) + ((lane >> 2) & 3);
+}
+template <int SHAPE>
+MFL_HD constexpr int tr_r(int lane) {
+  return (16 * (lane >> 4)) % Shape<SHAPE>::MN + 4 * (lane & 3);
+}
+template <int SHAPE>
+constexpr bool tr_reads_match_numeral() {
+  const AccLayout& L = operand_layout(SHAPE);
+  for (int lane = 0; lane < 64; ++lane)
+    for (int i = 0; i < 8; ++i) {
+      const int src = tr_src_lane(lane, i & 3);
+      const int k = tr_k<SHAPE>(src) + 4 * (i >> 2), r = tr_r<SHAPE>(src) + tr_src_elem(lane);
+      if (r != acc_row(L, lane, i) || k != acc_col(L, lane, i)) return false;
+    }
+  return true;
+}
+static_assert(tr_reads_match_numeral<0>() && tr_reads_match_numeral<1>(),
+              "transpose fragment reads disagree with the operand numerals");
+
+// Offsets of the reads relative to a lane's base address: read h of fragment f
+// in MFMA K step kk.  The bits they set are never set in a lane's base (k, r),
+// so adding is exact (checked below).
+template <int SHAPE>
+MFL_HD constexpr int kmaj_step(int kk, int h, int f) {
+  return lds_elemKM<SHAPE>(kk * Shape<SHAPE>::K + 4 * h, f * Shape<SHAPE>::MN);
+}
+
+// For every lane, K step, read and fragment origin (wave column r0, a multiple
+// of 64): the read lands on the element the lane needs, at base + kmaj_step; and
+// within each phase (lanes 0-31, 32-63) no two lanes touch one 4-byte bank at
+// different addresses.
+template <int SHAPE, int R, int NF>
+constexpr bool kmaj_reads_ok() {
+  constexpr int MN = Shape<SHAPE>::MN, KM = Shape<SHAPE>::K;
+  for (int r0 = 0; r0 < R; r0 += 64)
+    for (int lane = 0; lane < 64; ++lane) {
+      const int k = tr_k<SHAPE>(lane), r = r0 + tr_r<SHAPE>(lane);
+      for (int kk = 0; kk < 64 / KM; ++kk)
+        for (int h = 0; h < 2; ++h)
+          for (int f = 0; f < NF; ++f)
+            if (lds_elemKM<SHAPE>(k + kk * KM + 4 * h, r + f * MN) !=
+                lds_elemKM<SHAPE>(k, r) + kmaj_step<SHAPE>(kk, h, f))
+              return false;
+    }
+  for (int r0 = 0; r0 < R; r0 += MN)
+    for (int h = 0; h < 2; ++h)
+      for (int phase = 0; phase < 2; ++phase) {
+        int owner[64] = {};  // 1 + the dword address that each bank serves in this phase
+        for (int lane = 32 * phase; lane < 32 * phase + 32; ++lane) {
+          const int dw = lds_elemKM<SHAPE>(tr_k<SHAPE>(lane) + 4 * h, r0 + tr_r<SHAPE>(lane)) / 2;
+          for (int d = dw; d < dw + 2; ++d) {
+            if (owner[d % 64] != 0 && owner[d % 64] != d + 1) return false;
+            owner[d % 64] = d + 1;
+          }
+        }
+      }
+  return true;
+}
+static_assert(kmaj_reads_ok<0, 128, 4>() && kmaj_reads_ok<0, 256, 4>() && kmaj_reads_ok<1, 128, 2>() &&
+                  kmaj_reads_ok<1, 256, 2>(),
+              "k-major tile: transpose reads conflict or are not immediate offsets");
+
+// Per-lane base offset of a wave's fragments in a k-major tile; fragment f
+// covers columns row0 + f*MN .. +MN (row0 a multiple of 64).
+template <int SHAPE>
+struct KmFrag {
+  int off;
+  __device__ __forceinline__ KmFrag(int row0, int lane)
+      : off(lds_elemKM<SHAPE>(tr_k<SHAPE>(lane), row0 + tr_r<SHAPE>(lane))) {}
+};
+
+// Operand fragment f of MFMA K step kk, from a K-contiguous or a k-major tile.
+template <int SHAPE, int BK>
+__device__ __forceinline__ u32x4 frag_read(const uint16_t* s, const FragOffsets<SHAPE, BK>& o, int kk, int f) {
+  return lds_read16(s, o.off[kk] + f * Shape<SHAPE>::MN * BK);
+}
+template <int SHAPE>
+__device__ __forceinline__ u32x4 frag_read(const uint16_t* s, const KmFrag<SHAPE>& o, int kk, int f) {
+  return lds_read_tr(s, o.off + kmaj_step<SHAPE>(kk, 0, f), kmaj_step<SHAPE>(0, 1, 0));
+}
+
 // One BK-deep slab of the wave's TM x TN grid of MFMA tiles: for each MFMA K
 // step, read the A and B fragments from LDS and accumulate into registers.
-template <int SHAPE, int DT, int TM, int TN, int BK>
-__device__ __forceinline__ void mma_slab(const uint16_t* sA, const uint16_t* sB, const FragOffsets<SHAPE, BK>& fa,
-                                         const FragOffsets<SHAPE, BK>& fb,
+template <int SHAPE, int DT, int TM, int TN, int BK, class RA, class RB>
+__device__ __forceinline__ void mma_slab(const uint16_t* sA, const uint16_t* sB, const RA& fa, const RB& fb,
                                          typename Shape<SHAPE>::Acc (&acc)[TM][TN]) {
-  constexpr int MN = Shape<SHAPE>::MN;
 #pragma unroll
-  for (int kk = 0; kk < FragOffsets<SHAPE, BK>::KSTEPS; ++kk) {
+  for (int kk = 0; kk < BK / Shape<SHAPE>::K; ++kk) {
     u32x4 a[TM], b[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = lds_read16(sA, fa.off[kk] + i * MN * BK);
+    for (int i = 0; i < TM; ++i) a[i] = frag_read(sA, fa, kk, i);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = lds_read16(sB, fb.off[kk] + j * MN * BK);
+    for (int j = 0; j < TN; ++j) b[j] = frag_read(sB, fb, kk, j);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll

@@ -5,6 +5,8 @@
 // is in flight while the current one feeds the MFMAs), the fp32 accumulators
 // stay in registers for the whole loop, and the tile is stored once at the end
 // (Warp issue #1965, "Proposed change" and "Design consequences").
+#include <type_traits>
+
 #include "gemm_core.hpp"
 
 namespace mfl {
@@ -78,27 +80,76 @@ static int launch_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, f
 }
 
 // ---------------------------------------------------------------------------
-// Fast path: both operands K-contiguous, M % BM == 0, N % BN == 0, K % 64 == 0.
+// Fast path: M % BM == 0, N % BN == 0, K % 64 == 0, either operand order.
 // Global -> LDS moves use the CDNA4 direct-to-LDS buffer load
 // (buffer_load_dwordx4 ... lds): one wave instruction writes 64 x 16 bytes to
-// consecutive LDS addresses, so a wave fills 8 rows of a 128-byte-per-row tile
-// with no staging registers.  The swizzle is applied on the source side: the
-// lane that lands in physical chunk p of row r fetches logical chunk p ^ swz(r).
-// Per-lane state is one 32-bit offset per operand; the row step of each load
-// instruction and the K step are uniform scalar offsets.  Sixteen waves (four
-// per SIMD, 64 x 64 outputs each) let one wave's MFMAs run while another waits
-// on LDS or on the barrier; at 256 x 256 x 64 the ds_read_b128 fragment traffic
-// (4 LDS cycles each, conflict free) stays below the MFMA time.
+// consecutive LDS addresses, with no staging registers.  The swizzle is applied
+// on the source side: the lane that lands in physical chunk p of a tile row
+// fetches logical chunk p ^ swizzle(row).  Per-lane state is one 32-bit offset
+// per operand; the row step of each load instruction and the K step are uniform
+// scalar offsets.  Sixteen waves (four per SIMD, 64 x 64 outputs each) let one
+// wave's MFMAs run while another waits on LDS or on the barrier; at
+// 256 x 256 x 64 the fragment traffic (conflict free) stays below the MFMA time.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Direct-to-LDS loads of one operand's R x 64 slab per stage.
+//   K-contiguous (A row-major, B column-major): R rows of 64 K values, 128 bytes
+//     each, chunk XOR swz<64>(row); a load instruction fills 8 rows.
+//   k-major (A column-major, B row-major): the kmaj_chunk layout; a load
+//     instruction fills 64 consecutive chunks, 8 K rows x 128 contiguous bytes.
+// Load instruction i of wave w fills bytes (i*NW + w)*1024 .. +1024 of the slab.
+template <int SHAPE, int R, int NW, bool KMAJOR>
+struct DmaOperand {
+  static constexpr int INSTR = R / 8 / NW;
+  static_assert(INSTR * 8 * NW == R, "slab must split into whole wave loads");
+  // K-contiguous: every load instruction of a wave starts at the same row mod 16,
+  // so the swizzle — and the per-lane offset — is the same for all of them.
+  static_assert(KMAJOR || (NW * 8) % 16 == 0, "per-lane swizzle must be load-invariant");
+  static_assert(!KMAJOR || ((NW & (NW - 1)) == 0 && (R == 128 || R == 256)), "k-major slab shape");
+  rsrc_t rs;
+  uint32_t voff, ld2;
+
+  // X: the operand; r0: first M (or N) index of the tile; ld: leading dimension.
+  __device__ __forceinline__ DmaOperand(const uint16_t* X, uint32_t ld, int r0, int K, int wave, int lane) {
+    ld2 = ld * 2u;
+    if constexpr (KMAJOR) {
+      rs = make_rsrc(X + r0, (uint32_t)K * ld2);
+      // chunk (i*NW + wave)*64 + lane: the bits of i, wave and lane are disjoint
+      // and the layout permutes bits, so their (k, r) offsets add.
+      int k = 0, r = 0;
+      kmaj_coords<SHAPE>(wave * 64 + lane, &k, &r);
+      voff = (uint32_t)k * ld2 + (uint32_t)r * 2u;
+    } else {
+      rs = make_rsrc(X + (int64_t)r0 * ld, (uint32_t)R * ld2);
+      const int row = wave * 8 + (lane >> 3);
+      voff = (uint32_t)row * ld2 + (uint32_t)(((lane & 7) ^ swz<64>(row)) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(uint16_t* slab, int wave, int k0) const {
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      uint32_t soff;
+      if constexpr (KMAJOR) {
+        int ki = 0, ri = 0;
+        kmaj_coords<SHAPE>(i * NW * 64, &ki, &ri);
+        soff = (uint32_t)(ki + k0) * ld2 + (uint32_t)ri * 2u;
+      } else {
+        soff = (uint32_t)(i * NW * 8) * ld2 + (uint32_t)k0 * 2u;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(slab + (i * NW + wave) * 512), 16, voff, soff, 0, 0);
+    }
+  }
+};
+
 // STAGES-deep ring of LDS stages: stage kt+STAGES-1 is requested while stage kt
 // feeds the MFMAs.  One barrier per K step both publishes stage kt (every
 // wave's loads for it have landed) and retires stage kt-1, whose buffer the
-// new request reuses.
-template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT, int STAGES>
+// new request reuses.  AKM / BKM: A column-major / B row-major (k-major slabs,
+// fragments read with the transpose read).
+template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT, int STAGES, bool AKM, bool BKM>
 __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t* __restrict__ A,
                                                                    const uint16_t* __restrict__ B,
                                                                    float* __restrict__ C, uint32_t lda, uint32_t ldb,
@@ -110,12 +161,13 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
   constexpr int MN = Shape<SHAPE>::MN;
   constexpr int TM = WM / MN, TN = WN / MN;
   constexpr int STAGE = (BM + BN) * BK;
-  constexpr int A_INSTR = BM / 8 / NW, B_INSTR = BN / 8 / NW;
-  constexpr int LOADS = A_INSTR + B_INSTR;
-  static_assert(A_INSTR * 8 * NW == BM && B_INSTR * 8 * NW == BN, "tile rows must split into 8-row wave loads");
-  static_assert((NW % 2) == 0, "per-lane swizzle is load-invariant only for an even number of waves");
+  using DA = DmaOperand<SHAPE, BM, NW, AKM>;
+  using DB = DmaOperand<SHAPE, BN, NW, BKM>;
+  constexpr int LOADS = DA::INSTR + DB::INSTR;
   static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "vmcnt range");
   using Acc = typename Shape<SHAPE>::Acc;
+  using RA = std::conditional_t<AKM, KmFrag<SHAPE>, FragOffsets<SHAPE, BK>>;
+  using RB = std::conditional_t<BKM, KmFrag<SHAPE>, FragOffsets<SHAPE, BK>>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE];
 
@@ -126,29 +178,15 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr0 = (wave / WGN) * WM, wc0 = (wave % WGN) * WN;
 
-  // Buffers start at the workgroup's first row of A and of B (column of B).
-  const rsrc_t ra = make_rsrc(A + (int64_t)row0 * lda, (uint32_t)BM * lda * 2u);
-  const rsrc_t rb = make_rsrc(B + (int64_t)col0 * ldb, (uint32_t)BN * ldb * 2u);
-  // Load instruction i of this wave fills tile rows (i*NW + wave)*8 .. +8; lane l
-  // writes row +l/8, physical chunk l%8.  With NW even, (row mod 16) — and so
-  // the swizzle — is the same for every i, so one per-lane offset serves all.
-  const int lrow = wave * 8 + (lane >> 3);
-  const uint32_t va = (uint32_t)lrow * lda * 2u + (uint32_t)(((lane & 7) ^ swz<BK>(lrow)) << 4);
-  const uint32_t vb = (uint32_t)lrow * ldb * 2u + (uint32_t)(((lane & 7) ^ swz<BK>(lrow)) << 4);
-
+  const DA da(A, lda, row0, K, wave, lane);
+  const DB db(B, ldb, col0, K, wave, lane);
   auto issue = [&](int stage, int k0) {
-    uint16_t* base = lds + stage * STAGE + wave * 8 * BK;
-#pragma unroll
-    for (int i = 0; i < A_INSTR; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + i * NW * 8 * BK), 16, va,
-                                               (uint32_t)(i * NW * 8) * lda * 2u + (uint32_t)k0 * 2u, 0, 0);
-#pragma unroll
-    for (int i = 0; i < B_INSTR; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(base + BM * BK + i * NW * 8 * BK), 16, vb,
-                                               (uint32_t)(i * NW * 8) * ldb * 2u + (uint32_t)k0 * 2u, 0, 0);
+    da.issue(lds + stage * STAGE, wave, k0);
+    db.issue(lds + stage * STAGE + BM * BK, wave, k0);
   };
 
-  const FragOffsets<SHAPE, BK> fa(wr0, lane), fb(wc0, lane);
+  const RA fa(wr0, lane);
+  const RB fb(wc0, lane);
   Acc acc[TM][TN];
   zero_acc<SHAPE, TM, TN>(acc);
 
@@ -176,11 +214,11 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
     store_acc_rsrc<SHAPE, TM, TN, false>(rc, ldc, lane, acc);
 }
 
-template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT, int STAGES = 2>
+template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT, bool AKM, bool BKM, int STAGES = 2>
 static int launch_fast(const void* a, int64_t lda, const void* b, int64_t ldb, float* c, int64_t ldc, int M, int N,
                        int K, int accumulate, hipStream_t stream) {
   const int tiles_m = M / BM, tiles_n = N / BN;
-  hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WGM, WGN, SHAPE, DT, STAGES>), dim3(tiles_m * tiles_n),
+  hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WGM, WGN, SHAPE, DT, STAGES, AKM, BKM>), dim3(tiles_m * tiles_n),
                      dim3(WGM * WGN * 64), 0,
                      stream, (const uint16_t*)a, (const uint16_t*)b, c, (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, K,
                      tiles_m, tiles_n, accumulate);
@@ -196,42 +234,56 @@ static int launch_generic(const void* a, int64_t lda, const void* b, int64_t ldb
   return launch_gemm<128, 128, 64, 2, 2, 0, DT, AK, BKC, true>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
 }
 
-// The buffer offsets of the fast path are 32-bit: the byte extent of a 256-row
-// panel of A, B and of C must stay below 4 GiB.
-static bool fast_fits(int64_t lda, int64_t ldb, int64_t ldc) {
+// The buffer offsets of the fast path are 32-bit.  A K-contiguous operand's
+// buffer is one tile panel (rows x ld elements, rows = 256 at most); a k-major
+// operand's buffer spans all K rows (K x ld elements); C's is 256 rows of ldc.
+static bool fast_fits(bool kmajor, int64_t ld, int64_t K) {
   const int64_t lim = (int64_t)1 << 32;
-  return 256 * lda * 2 < lim && 256 * ldb * 2 < lim && 256 * ldc * 4 < lim;
+  return kmajor ? K * ld * 2 < lim : 256 * ld * 2 < lim;
+}
+
+template <int DT, bool AKM, bool BKM>
+static int dispatch_fast(int shape, const void* a, int64_t lda, const void* b, int64_t ldb, float* c, int64_t ldc,
+                         int M, int N, int K, int accumulate, hipStream_t s) {
+  // The largest tile that still gives the chip at least 128 workgroups:
+  // 256 x 256 (16 waves of 64 x 64), 128 x 128 (4 waves of 64 x 64), or for
+  // small problems with K-contiguous operands 64 x 64 (2 waves of 32 x 64),
+  // where a single big tile would leave all but a few CUs idle.
+  const auto count = [&](int t) { return (int64_t)(M / t) * (N / t); };
+  const bool s32 = shape == MFL_MFMA_32X32X16;
+  if (M % 256 == 0 && N % 256 == 0 && count(256) >= 128)
+    return s32 ? launch_fast<256, 256, 4, 4, 1, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)
+               : launch_fast<256, 256, 4, 4, 0, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  if (M % 128 == 0 && N % 128 == 0 && (count(128) >= 128 || AKM || BKM))
+    return s32 ? launch_fast<128, 128, 2, 2, 1, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)
+               : launch_fast<128, 128, 2, 2, 0, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  if constexpr (!AKM && !BKM)
+    if (M % 64 == 0 && N % 64 == 0)
+      return s32 ? launch_fast<64, 64, 2, 1, 1, DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)
+                 : launch_fast<64, 64, 2, 1, 0, DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  return MFL_EUNSUPPORTED;  // not reached: the caller checked the sizes
+}
+
+// Whether dispatch_fast has a tile for these sizes.
+static bool fast_tiles(bool any_kmajor, int M, int N) {
+  if (M % 128 == 0 && N % 128 == 0) return true;
+  return !any_kmajor && M % 64 == 0 && N % 64 == 0;
 }
 
 template <int DT>
 static int dispatch(int shape, const void* a, int64_t lda, int oa, const void* b, int64_t ldb, int ob, float* c,
                     int64_t ldc, int M, int N, int K, int accumulate, hipStream_t s) {
-  const bool ak = oa == MFL_ROW_MAJOR, bk = ob == MFL_COL_MAJOR;
-  if (ak && bk && K % 64 == 0 && fast_fits(lda, ldb, ldc)) {
-    // The largest tile that still gives the chip at least 128 workgroups:
-    // 256 x 256 (16 waves of 64 x 64), 128 x 128 (4 waves of 64 x 64), or for
-    // small problems 64 x 64 (2 waves of 32 x 64), where a single big tile would
-    // leave all but a few CUs idle.
-    const auto count = [&](int t) { return (int64_t)(M / t) * (N / t); };
-    if (M % 256 == 0 && N % 256 == 0 && count(256) >= 128) {
-      if (shape == MFL_MFMA_32X32X16)
-        return launch_fast<256, 256, 4, 4, 1, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-      return launch_fast<256, 256, 4, 4, 0, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-    }
-    if (M % 128 == 0 && N % 128 == 0 && count(128) >= 128) {
-      if (shape == MFL_MFMA_32X32X16)
-        return launch_fast<128, 128, 2, 2, 1, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-      return launch_fast<128, 128, 2, 2, 0, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-    }
-    if (M % 64 == 0 && N % 64 == 0) {
-      if (shape == MFL_MFMA_32X32X16)
-        return launch_fast<64, 64, 2, 1, 1, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-      return launch_fast<64, 64, 2, 1, 0, DT>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-    }
+  const bool akm = oa == MFL_COL_MAJOR, bkm = ob == MFL_ROW_MAJOR;
+  if (K % 64 == 0 && fast_tiles(akm || bkm, M, N) && fast_fits(akm, lda, K) && fast_fits(bkm, ldb, K) &&
+      256 * ldc * 4 < ((int64_t)1 << 32)) {
+    if (!akm && !bkm) return dispatch_fast<DT, false, false>(shape, a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+    if (!akm) return dispatch_fast<DT, false, true>(shape, a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+    if (!bkm) return dispatch_fast<DT, true, false>(shape, a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+    return dispatch_fast<DT, true, true>(shape, a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
   }
-  if (ak && bk) return launch_generic<DT, true, true>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-  if (ak) return launch_generic<DT, true, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-  if (bk) return launch_generic<DT, false, true>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  if (!akm && !bkm) return launch_generic<DT, true, true>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  if (!akm) return launch_generic<DT, true, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  if (!bkm) return launch_generic<DT, false, true>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
   return launch_generic<DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
 }
 

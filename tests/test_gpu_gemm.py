@@ -183,3 +183,62 @@ def test_fast_path_tile_sizes(mnk, accumulate, shape, fmt):
     ref = R.gemm_ref(a, bt, fmt) + (c0.astype(np.float64) if accumulate else 0.0)
     assert not np.isnan(c).any()
     assert R.rel_error(c, ref) <= TOL
+
+
+# K-strided operands (A column-major, B row-major) take the fast path through
+# k-major LDS slabs read with the gfx950 transpose read.  Every lane still holds
+# the K positions of the operand numeral and the MFMA sequence is the same, so
+# each order gives the same bits as the K-contiguous launch on the same values.
+ORDERS = [(mfl.ROW_MAJOR, mfl.COL_MAJOR), (mfl.ROW_MAJOR, mfl.ROW_MAJOR), (mfl.COL_MAJOR, mfl.COL_MAJOR),
+          (mfl.COL_MAJOR, mfl.ROW_MAJOR)]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [0, 1])
+@pytest.mark.parametrize("mnk,accumulate", [((4096, 4096, 128), 0),   # 256 x 256 tiles
+                                            ((2048, 1024, 192), 0),   # 128 x 128 tiles
+                                            ((256, 384, 320), 1),     # 128 x 128 (k-major), 64 x 64 (K-contiguous)
+                                            ((128, 128, 64), 0)])     # one tile, one K step
+def test_fast_path_all_orders_bit_identical(mnk, accumulate, shape, fmt):
+    m, n, k = mnk
+    rng = np.random.default_rng(3 * m + n + k + shape)
+    a = rng.uniform(-1, 1, (m, k)).astype(np.float32)
+    b = rng.uniform(-1, 1, (k, n)).astype(np.float32)
+    c0 = rng.standard_normal((m, n)).astype(np.float32) if accumulate else None
+    ref = R.gemm_ref(a, np.ascontiguousarray(b.T), fmt) + (c0.astype(np.float64) if accumulate else 0.0)
+    first = None
+    for oa, ob in ORDERS:
+        say("gemm fast orders", m, n, k, shape, fmt, oa, ob)
+        c = run_gemm(fmt, a, b, oa, ob, shape=shape, accumulate=accumulate, c0=c0)
+        assert not np.isnan(c).any()
+        assert R.rel_error(c, ref) <= TOL
+        if first is None:
+            first = c
+        else:
+            assert np.array_equal(c.view(np.uint32), first.view(np.uint32)), (oa, ob)
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+@pytest.mark.parametrize("orders", ORDERS[1:])
+def test_dense_4096_bf16_other_orders(orders, shape):
+    """The benchmark's 4096^3 bf16 GEMM with K-strided operands (ld 4160, NaN
+    padding): bit-identical to the K-contiguous launch on the same values."""
+    a, bt = inputs.gemm_dense()
+    n = 4096
+
+    def padded(x):
+        s = np.full((n, 4160), np.nan, np.float32)
+        s[:, :n] = x
+        return s
+
+    oa, ob = orders
+    sa = a if oa == mfl.ROW_MAJOR else padded(a[:, :n].T)
+    sb = bt if ob == mfl.COL_MAJOR else padded(bt[:, :n].T)
+    say("dense 4096^3 orders", oa, ob, shape)
+    ref = torch.empty((n, n), device=device())
+    mfl.gemm_tile_mma_shape(shape, mfl.BF16, n, n, n, q16(a, "bf16"), 4160, mfl.ROW_MAJOR, q16(bt, "bf16"), 4160,
+                            mfl.COL_MAJOR, ref, n, 0, stream())
+    c = torch.full((n, n), np.nan, device=device())
+    mfl.gemm_tile_mma_shape(shape, mfl.BF16, n, n, n, q16(sa, "bf16"), 4160, oa, q16(sb, "bf16"), 4160, ob, c, n, 0,
+                            stream())
+    assert torch.equal(c.view(torch.int32), ref.view(torch.int32))
