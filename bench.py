@@ -256,8 +256,16 @@ def split(torch, mfl, inputs, stream, dev, out):
             "us": round(ms * 1e3, 1), "useful_tflops": round(2 * 4096 ** 3 / ms / 1e9, 1),
             "mfma_tflops": round(mf, 1), "frac_mfma_peak": round(mf / PEAK_BF16_TFLOPS, 4),
             "split_on_load_us": round(ms_load * 1e3, 1)}
+    # 3 chains with A column-major and B row-major (k-major planes, transpose reads)
+    dat = torch.from_numpy(np.ascontiguousarray(a.T)).to(dev)
+    dbt = torch.from_numpy(np.ascontiguousarray(bt.T)).to(dev)
+    ms = best_of(lambda: mfl.gemm_split_fp32_ws(mfl.BF16, 4096, 4096, 4096, dat, 4096, 1, 1, dbt, 4096, 0, 1, 3, 0, c,
+                                                4096, 0, ws, wsb, stream), stream, rounds=2, per=5)
+    mf = 3 * 2 * 4096 ** 3 / ms / 1e9
+    sp["chains3_A_col_B_row"] = {"us": round(ms * 1e3, 1), "useful_tflops": round(2 * 4096 ** 3 / ms / 1e9, 1),
+                                 "mfma_tflops": round(mf, 1), "frac_mfma_peak": round(mf / PEAK_BF16_TFLOPS, 4)}
     out["split_4096"] = sp
-    del da, db, c, ws
+    del da, db, dat, dbt, c, ws
 
 
 def attention(torch, mfl, inputs, stream, dev, out):

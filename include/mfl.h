@@ -245,11 +245,12 @@ MFL_API int gemm_split_fp32(int piece, int64_t m, int64_t n, int64_t k,
                     void *stream);
 
 /* Workspace for gemm_split_fp32_ws: the bytes of the four 16-bit planes
- * (hi and lo of A and of B, each operand rows x ld, 256-byte aligned) when the
- * planes path applies — both operands MFL_SPLIT, A row-major and B
- * column-major, m % 128 == 0, n % 128 == 0, k % 64 == 0 (k > 0), lda % 8 == 0,
- * ldb % 8 == 0 — and 0 otherwise (then gemm_split_fp32_ws runs the
- * split-on-load kernel, which needs none).  MFL_EINVAL on NULL or unknown
+ * (hi and lo of A and of B, each in its operand's storage shape — A: m rows
+ * row-major, k rows column-major; B: n rows column-major, k rows row-major —
+ * of ld elements, 256-byte aligned) when the planes path applies — both
+ * operands MFL_SPLIT, any orders, m % 128 == 0, n % 128 == 0, k % 64 == 0
+ * (k > 0), lda % 8 == 0, ldb % 8 == 0, buffers within 4 GiB — and 0 otherwise
+ * (then gemm_split_fp32_ws runs the split-on-load kernel, which needs none).  MFL_EINVAL on NULL or unknown
  * orders / modes, MFL_EOVERFLOW if the size does not fit int64. */
 MFL_API int gemm_split_fp32_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t lda, int order_a,
                                             int mode_a, int64_t ldb, int order_b, int mode_b, int64_t ldc,

@@ -141,14 +141,14 @@ MFL_HD constexpr int kmaj_step(int kk, int h, int f) {
   return lds_elemKM<SHAPE>(kk * Shape<SHAPE>::K + 4 * h, f * Shape<SHAPE>::MN);
 }
 
-// For every lane, K step, read and fragment origin (wave column r0, a multiple
-// of 64): the read lands on the element the lane needs, at base + kmaj_step; and
-// within each phase (lanes 0-31, 32-63) no two lanes touch one 4-byte bank at
-// different addresses.
-template <int SHAPE, int R, int NF>
+// For every lane, K step, read and fragment of a wave whose NF fragments start
+// at r0 (a multiple of WS): the read lands on the element the lane needs, at
+// base + kmaj_step; and within each phase (lanes 0-31, 32-63) no two lanes
+// touch one 4-byte bank at different addresses.
+template <int SHAPE, int R, int WS, int NF>
 constexpr bool kmaj_reads_ok() {
   constexpr int MN = Shape<SHAPE>::MN, KM = Shape<SHAPE>::K;
-  for (int r0 = 0; r0 < R; r0 += 64)
+  for (int r0 = 0; r0 < R; r0 += WS)
     for (int lane = 0; lane < 64; ++lane) {
       const int k = tr_k<SHAPE>(lane), r = r0 + tr_r<SHAPE>(lane);
       for (int kk = 0; kk < 64 / KM; ++kk)
@@ -172,14 +172,12 @@ constexpr bool kmaj_reads_ok() {
       }
   return true;
 }
-static_assert(kmaj_reads_ok<0, 128, 4>() && kmaj_reads_ok<0, 256, 4>() && kmaj_reads_ok<1, 128, 2>() &&
-                  kmaj_reads_ok<1, 256, 2>(),
-              "k-major tile: transpose reads conflict or are not immediate offsets");
-
-// Per-lane base offset of a wave's fragments in a k-major tile; fragment f
-// covers columns row0 + f*MN .. +MN (row0 a multiple of 64).
-template <int SHAPE>
+// Per-lane base offset of a wave's NF fragments in a k-major tile of R columns;
+// fragment f covers columns row0 + f*MN .. +MN, row0 being a multiple of WS.
+template <int SHAPE, int R, int WS, int NF>
 struct KmFrag {
+  static_assert(NF * Shape<SHAPE>::MN <= WS && kmaj_reads_ok<SHAPE, R, WS, NF>(),
+                "k-major tile: transpose reads conflict or are not immediate offsets");
   int off;
   __device__ __forceinline__ KmFrag(int row0, int lane)
       : off(lds_elemKM<SHAPE>(tr_k<SHAPE>(lane), row0 + tr_r<SHAPE>(lane))) {}
@@ -190,8 +188,8 @@ template <int SHAPE, int BK>
 __device__ __forceinline__ u32x4 frag_read(const uint16_t* s, const FragOffsets<SHAPE, BK>& o, int kk, int f) {
   return lds_read16(s, o.off[kk] + f * Shape<SHAPE>::MN * BK);
 }
-template <int SHAPE>
-__device__ __forceinline__ u32x4 frag_read(const uint16_t* s, const KmFrag<SHAPE>& o, int kk, int f) {
+template <int SHAPE, int R, int WS, int NF>
+__device__ __forceinline__ u32x4 frag_read(const uint16_t* s, const KmFrag<SHAPE, R, WS, NF>& o, int kk, int f) {
   return lds_read_tr(s, o.off + kmaj_step<SHAPE>(kk, 0, f), kmaj_step<SHAPE>(0, 1, 0));
 }
 
@@ -213,6 +211,62 @@ __device__ __forceinline__ void mma_slab(const uint16_t* sA, const uint16_t* sB,
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma<SHAPE, DT>(a[i], b[j], acc[i][j]);
   }
 }
+
+// Wait until at most N of this wave's vector-memory operations (the
+// direct-to-LDS loads included) are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Direct-to-LDS loads of one operand's R x 64 slab per stage.
+//   K-contiguous (A row-major, B column-major): R rows of 64 K values, 128 bytes
+//     each, chunk XOR swz<64>(row); a load instruction fills 8 rows.
+//   k-major (A column-major, B row-major): the kmaj_chunk layout; a load
+//     instruction fills 64 consecutive chunks, 8 K rows x 128 contiguous bytes.
+// Load instruction i of wave w fills bytes (i*NW + w)*1024 .. +1024 of the slab.
+template <int SHAPE, int R, int NW, bool KMAJOR>
+struct DmaOperand {
+  static constexpr int INSTR = R / 8 / NW;
+  static_assert(INSTR * 8 * NW == R, "slab must split into whole wave loads");
+  // K-contiguous: every load instruction of a wave starts at the same row mod 16,
+  // so the swizzle — and the per-lane offset — is the same for all of them.
+  static_assert(KMAJOR || (NW * 8) % 16 == 0, "per-lane swizzle must be load-invariant");
+  static_assert(!KMAJOR || ((NW & (NW - 1)) == 0 && (R == 128 || R == 256)), "k-major slab shape");
+  rsrc_t rs;
+  uint32_t voff, ld2;
+
+  // X: the operand; r0: first M (or N) index of the tile; ld: leading dimension.
+  __device__ __forceinline__ DmaOperand(const uint16_t* X, uint32_t ld, int r0, int K, int wave, int lane) {
+    ld2 = ld * 2u;
+    if constexpr (KMAJOR) {
+      rs = make_rsrc(X + r0, (uint32_t)K * ld2);
+      // chunk (i*NW + wave)*64 + lane: the bits of i, wave and lane are disjoint
+      // and the layout permutes bits, so their (k, r) offsets add.
+      int k = 0, r = 0;
+      kmaj_coords<SHAPE>(wave * 64 + lane, &k, &r);
+      voff = (uint32_t)k * ld2 + (uint32_t)r * 2u;
+    } else {
+      rs = make_rsrc(X + (int64_t)r0 * ld, (uint32_t)R * ld2);
+      const int row = wave * 8 + (lane >> 3);
+      voff = (uint32_t)row * ld2 + (uint32_t)(((lane & 7) ^ swz<64>(row)) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(uint16_t* slab, int wave, int k0) const {
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      uint32_t soff;
+      if constexpr (KMAJOR) {
+        int ki = 0, ri = 0;
+        kmaj_coords<SHAPE>(i * NW * 64, &ki, &ri);
+        soff = (uint32_t)(ki + k0) * ld2 + (uint32_t)ri * 2u;
+      } else {
+        soff = (uint32_t)(i * NW * 8) * ld2 + (uint32_t)k0 * 2u;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(slab + (i * NW + wave) * 512), 16, voff, soff, 0, 0);
+    }
+  }
+};
 
 // Epilogue: every accumulator value goes to C[(row0+row)*ldc + col0+col] with
 // (row, col) from the instruction's accumulator layout — one store per value.

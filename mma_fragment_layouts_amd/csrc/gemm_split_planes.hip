@@ -15,16 +15,16 @@
 // MFMAs.  For every accumulator the MFMAs arrive in the same order as in the
 // split-on-load kernel (K steps ascending; within one, hh, hl, lh, ll), and the
 // chains are summed the same way, so both kernels give bit-identical results.
+#include <type_traits>
+
 #include "gemm_split.hpp"
 
 namespace mfl {
 
-template <int N>
-__device__ __forceinline__ void planes_wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-template <int DT, class P>
+// AKM / BKM: A column-major / B row-major — those planes are staged k-major
+// and read with the transpose read, as in the dense fast path; the MFMAs and
+// their order do not change, so every operand order gives the same bits.
+template <int DT, class P, bool AKM, bool BKM>
 __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* __restrict__ Ah,
                                                                 const uint16_t* __restrict__ Al,
                                                                 const uint16_t* __restrict__ Bh,
@@ -38,10 +38,12 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
   constexpr int TM = WM / MN, TN = WN / MN;
   constexpr int PLANE = BM * BK;                   // one plane's slab (BM == BN), 16-bit elements
   constexpr int STAGE = 4 * PLANE;                 // A_hi | A_lo | B_hi | B_lo
-  constexpr int PER = BM / 8 / NW;                 // 8-row wave loads per plane and wave
-  constexpr int LOADS = 4 * PER;
-  static_assert(PER * 8 * NW == BM && BM == BN, "plane rows must split into 8-row wave loads");
-  static_assert((NW % 2) == 0, "per-lane swizzle is load-invariant only for an even number of waves");
+  static_assert(BM == BN, "planes share one slab size");
+  using DA = DmaOperand<SHAPE, BM, NW, AKM>;
+  using DB = DmaOperand<SHAPE, BN, NW, BKM>;
+  static_assert(2 * (DA::INSTR + DB::INSTR) < 64, "vmcnt range");
+  using RA = std::conditional_t<AKM, KmFrag<SHAPE, BM, WM, TM>, FragOffsets<SHAPE, BK>>;
+  using RB = std::conditional_t<BKM, KmFrag<SHAPE, BN, WN, TN>, FragOffsets<SHAPE, BK>>;
   using Acc = typename Shape<SHAPE>::Acc;
 
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
@@ -53,31 +55,18 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr0 = (wave / WGN) * WM, wc0 = (wave % WGN) * WN;
 
-  const rsrc_t rah = make_rsrc(Ah + (int64_t)row0 * lda, (uint32_t)BM * lda * 2u);
-  const rsrc_t ral = make_rsrc(Al + (int64_t)row0 * lda, (uint32_t)BM * lda * 2u);
-  const rsrc_t rbh = make_rsrc(Bh + (int64_t)col0 * ldb, (uint32_t)BN * ldb * 2u);
-  const rsrc_t rbl = make_rsrc(Bl + (int64_t)col0 * ldb, (uint32_t)BN * ldb * 2u);
-  // Load i of this wave fills plane rows (i*NW + wave)*8 .. +8; lane l writes
-  // row +l/8, physical chunk l%8, fetching logical chunk (l%8) ^ swz(row).
-  const int lrow = wave * 8 + (lane >> 3);
-  const uint32_t va = (uint32_t)lrow * lda * 2u + (uint32_t)(((lane & 7) ^ swz<BK>(lrow)) << 4);
-  const uint32_t vb = (uint32_t)lrow * ldb * 2u + (uint32_t)(((lane & 7) ^ swz<BK>(lrow)) << 4);
-
+  const DA dah(Ah, lda, row0, K, wave, lane), dal(Al, lda, row0, K, wave, lane);
+  const DB dbh(Bh, ldb, col0, K, wave, lane), dbl(Bl, ldb, col0, K, wave, lane);
   auto issue = [&](int stage, int k0) {
-    uint16_t* base = lds + stage * STAGE + wave * 8 * BK;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const uint32_t sa = (uint32_t)(i * NW * 8) * lda * 2u + (uint32_t)k0 * 2u;
-      const uint32_t sb = (uint32_t)(i * NW * 8) * ldb * 2u + (uint32_t)k0 * 2u;
-      uint16_t* dst = base + i * NW * 8 * BK;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rah, (lds_ptr_t)(dst), 16, va, sa, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ral, (lds_ptr_t)(dst + PLANE), 16, va, sa, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbh, (lds_ptr_t)(dst + 2 * PLANE), 16, vb, sb, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbl, (lds_ptr_t)(dst + 3 * PLANE), 16, vb, sb, 0, 0);
-    }
+    uint16_t* st = lds + stage * STAGE;
+    dah.issue(st, wave, k0);
+    dal.issue(st + PLANE, wave, k0);
+    dbh.issue(st + 2 * PLANE, wave, k0);
+    dbl.issue(st + 3 * PLANE, wave, k0);
   };
 
-  const FragOffsets<SHAPE, BK> fa(wr0, lane), fb(wc0, lane);
+  const RA fa(wr0, lane);
+  const RB fb(wc0, lane);
   Acc acc[P::CHAINS][TM][TN];
 #pragma unroll
   for (int ch = 0; ch < P::CHAINS; ++ch) zero_acc<SHAPE, TM, TN>(acc[ch]);
@@ -87,22 +76,22 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
   for (int kt = 0; kt < KT; ++kt) {
     // this wave's loads of stage kt have landed; after the barrier every
     // wave's have, and stage kt-1 (the buffer refilled next) is retired
-    planes_wait_vmcnt<0>();
+    wait_vmcnt<0>();
     __syncthreads();
     if (kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * BK);
     const uint16_t* st = lds + (kt & 1) * STAGE;
 #pragma unroll
-    for (int kk = 0; kk < FragOffsets<SHAPE, BK>::KSTEPS; ++kk) {
+    for (int kk = 0; kk < BK / Shape<SHAPE>::K; ++kk) {
       u32x4 ah[TM], al[TM], bh[TN], bl[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        ah[i] = lds_read16(st, fa.off[kk] + i * MN * BK);
-        al[i] = lds_read16(st + PLANE, fa.off[kk] + i * MN * BK);
+        ah[i] = frag_read(st, fa, kk, i);
+        al[i] = frag_read(st + PLANE, fa, kk, i);
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        bh[j] = lds_read16(st + 2 * PLANE, fb.off[kk] + j * MN * BK);
-        bl[j] = lds_read16(st + 3 * PLANE, fb.off[kk] + j * MN * BK);
+        bh[j] = frag_read(st + 2 * PLANE, fb, kk, j);
+        bl[j] = frag_read(st + 3 * PLANE, fb, kk, j);
       }
 #pragma unroll
       for (int p = 0; p < P::NPROD; ++p)
@@ -116,7 +105,6 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
           }
     }
   }
-  static_assert(LOADS < 64, "vmcnt range");
   // Chains in plain fp32, the small ones first: c0 + (c1 + c2).
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -132,21 +120,22 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
     store_acc_rsrc<SHAPE, TM, TN, false>(rc, ldc, lane, acc[0]);
 }
 
-template <int DT, class P>
+template <int DT, class P, bool AKM, bool BKM>
 static int launch_planes(const uint16_t* ah, const uint16_t* al, const uint16_t* bh, const uint16_t* bl, float* c,
                          int64_t lda, int64_t ldb, int64_t ldc, int M, int N, int K, int accumulate, hipStream_t s) {
   const int tiles_m = M / 128, tiles_n = N / 128;
-  hipLaunchKernelGGL((gemm_split_planes_kernel<DT, P>), dim3(tiles_m * tiles_n), dim3(512), 0, s, ah, al, bh, bl, c,
-                     (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, K, tiles_m, tiles_n, accumulate);
+  hipLaunchKernelGGL((gemm_split_planes_kernel<DT, P, AKM, BKM>), dim3(tiles_m * tiles_n), dim3(512), 0, s, ah, al, bh,
+                     bl, c, (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, K, tiles_m, tiles_n, accumulate);
   return launch_status();
 }
 
-template <int DT>
+template <int DT, bool AKM, bool BKM>
 static int dispatch_planes(int chains, bool lolo, const uint16_t* ah, const uint16_t* al, const uint16_t* bh,
                            const uint16_t* bl, float* c, int64_t lda, int64_t ldb, int64_t ldc, int M, int N, int K,
                            int accumulate, hipStream_t s) {
-#define MFL_PLANES(CH, LL) \
-  return launch_planes<DT, Products<true, true, CH, LL>>(ah, al, bh, bl, c, lda, ldb, ldc, M, N, K, accumulate, s)
+#define MFL_PLANES(CH, LL)                                                                                       \
+  return launch_planes<DT, Products<true, true, CH, LL>, AKM, BKM>(ah, al, bh, bl, c, lda, ldb, ldc, M, N, K, \
+                                                                   accumulate, s)
   if (lolo) {
     if (chains == 1) MFL_PLANES(1, true);
     if (chains == 2) MFL_PLANES(2, true);
@@ -158,21 +147,43 @@ static int dispatch_planes(int chains, bool lolo, const uint16_t* ah, const uint
 #undef MFL_PLANES
 }
 
-static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
-
-// Plane sizes: A as m rows of lda, B as n rows (columns of B) of ldb, 16-bit.
-static int64_t planes_bytes(int64_t m, int64_t n, int64_t lda, int64_t ldb) {
-  return 2 * align256(m * lda * 2) + 2 * align256(n * ldb * 2);
+template <int DT>
+static int dispatch_planes_orders(bool akm, bool bkm, int chains, bool lolo, const uint16_t* ah, const uint16_t* al,
+                                  const uint16_t* bh, const uint16_t* bl, float* c, int64_t lda, int64_t ldb,
+                                  int64_t ldc, int M, int N, int K, int accumulate, hipStream_t s) {
+  if (!akm && !bkm)
+    return dispatch_planes<DT, false, false>(chains, lolo, ah, al, bh, bl, c, lda, ldb, ldc, M, N, K, accumulate, s);
+  if (!akm)
+    return dispatch_planes<DT, false, true>(chains, lolo, ah, al, bh, bl, c, lda, ldb, ldc, M, N, K, accumulate, s);
+  if (!bkm)
+    return dispatch_planes<DT, true, false>(chains, lolo, ah, al, bh, bl, c, lda, ldb, ldc, M, N, K, accumulate, s);
+  return dispatch_planes<DT, true, true>(chains, lolo, ah, al, bh, bl, c, lda, ldb, ldc, M, N, K, accumulate, s);
 }
 
-// The planes path takes both operands split and K contiguous, whole tiles, rows
-// of the planes 16-byte aligned, and 32-bit buffer offsets within a 128-row panel.
+static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+// Storage rows of an operand: A (m x k) has m rows of lda when row-major and k
+// rows when column-major; B (k x n) has n rows of ldb when column-major and k
+// rows when row-major.  The planes have the operand's storage shape.
+static int64_t rows_a(int64_t m, int64_t k, int order_a) { return order_a == MFL_ROW_MAJOR ? m : k; }
+static int64_t rows_b(int64_t n, int64_t k, int order_b) { return order_b == MFL_COL_MAJOR ? n : k; }
+static int64_t inner_a(int64_t m, int64_t k, int order_a) { return order_a == MFL_ROW_MAJOR ? k : m; }
+static int64_t inner_b(int64_t n, int64_t k, int order_b) { return order_b == MFL_COL_MAJOR ? k : n; }
+
+static int64_t planes_bytes(int64_t m, int64_t n, int64_t k, int64_t lda, int order_a, int64_t ldb, int order_b) {
+  return 2 * align256(rows_a(m, k, order_a) * lda * 2) + 2 * align256(rows_b(n, k, order_b) * ldb * 2);
+}
+
+// The planes path takes both operands split, whole tiles, rows of the planes
+// 16-byte aligned, and 32-bit buffer offsets: a K-contiguous operand's buffer is
+// one 128-row panel, a k-major operand's spans all k rows.
 static bool planes_apply(int64_t m, int64_t n, int64_t k, int64_t lda, int order_a, int mode_a, int64_t ldb,
                          int order_b, int mode_b, int64_t ldc) {
   const int64_t lim = (int64_t)1 << 32;
-  return mode_a == MFL_SPLIT && mode_b == MFL_SPLIT && order_a == MFL_ROW_MAJOR && order_b == MFL_COL_MAJOR &&
-         m % 128 == 0 && n % 128 == 0 && k % 64 == 0 && k > 0 && lda % 8 == 0 && ldb % 8 == 0 &&
-         128 * lda * 2 < lim && 128 * ldb * 2 < lim && 64 * ldc * 4 < lim;
+  if (mode_a != MFL_SPLIT || mode_b != MFL_SPLIT) return false;
+  if (m % 128 != 0 || n % 128 != 0 || k % 64 != 0 || k <= 0 || lda % 8 != 0 || ldb % 8 != 0) return false;
+  const int64_t pa = order_a == MFL_ROW_MAJOR ? 128 : k, pb = order_b == MFL_COL_MAJOR ? 128 : k;
+  return pa * lda * 2 < lim && pb * ldb * 2 < lim && 64 * ldc * 4 < lim;
 }
 
 }  // namespace mfl
@@ -191,8 +202,8 @@ extern "C" int gemm_split_fp32_workspace_bytes(int64_t m, int64_t n, int64_t k, 
     *bytes = 0;  // the split-on-load kernel runs; it needs no workspace
     return MFL_OK;
   }
-  if (m > INT64_MAX / 4 / lda || n > INT64_MAX / 4 / ldb) return MFL_EOVERFLOW;
-  *bytes = planes_bytes(m, n, lda, ldb);
+  if (rows_a(m, k, order_a) > INT64_MAX / 4 / lda || rows_b(n, k, order_b) > INT64_MAX / 4 / ldb) return MFL_EOVERFLOW;
+  *bytes = planes_bytes(m, n, k, lda, order_a, ldb, order_b);
   return MFL_OK;
 }
 
@@ -213,23 +224,27 @@ extern "C" int gemm_split_fp32_ws(int piece, int64_t m, int64_t n, int64_t k, co
   if (chains < 1 || chains > 3 || chains > 3 + lolo) return MFL_EINVAL;
   if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return MFL_EUNSUPPORTED;
   if (!a || !b || !c || !aligned16(a) || !aligned16(b) || ((uintptr_t)c & 3)) return MFL_EINVAL;
-  if (lda < k || ldb < k || ldc < n) return MFL_EINVAL;
-  if (m > INT64_MAX / 4 / lda || n > INT64_MAX / 4 / ldb || m > INT64_MAX / ldc) return MFL_EOVERFLOW;
-  if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < planes_bytes(m, n, lda, ldb)) return MFL_EINVAL;
+  const int64_t ra = rows_a(m, k, order_a), rb = rows_b(n, k, order_b);
+  if (lda < inner_a(m, k, order_a) || ldb < inner_b(n, k, order_b) || ldc < n) return MFL_EINVAL;
+  if (ra > INT64_MAX / 4 / lda || rb > INT64_MAX / 4 / ldb || m > INT64_MAX / ldc) return MFL_EOVERFLOW;
+  if (!workspace || ((uintptr_t)workspace & 255) ||
+      workspace_bytes < planes_bytes(m, n, k, lda, order_a, ldb, order_b))
+    return MFL_EINVAL;
   char* w = (char*)workspace;
   uint16_t* ah = (uint16_t*)w;
-  uint16_t* al = (uint16_t*)(w + align256(m * lda * 2));
-  uint16_t* bh = (uint16_t*)(w + 2 * align256(m * lda * 2));
-  uint16_t* bl = (uint16_t*)(w + 2 * align256(m * lda * 2) + align256(n * ldb * 2));
-  // Split exactly the elements an m x k (n x k) operand with that leading
-  // dimension spans, (rows - 1) * ld + k: the last row need not be padded.
+  uint16_t* al = (uint16_t*)(w + align256(ra * lda * 2));
+  uint16_t* bh = (uint16_t*)(w + 2 * align256(ra * lda * 2));
+  uint16_t* bl = (uint16_t*)(w + 2 * align256(ra * lda * 2) + align256(rb * ldb * 2));
+  // Split exactly the elements each operand's storage spans,
+  // (rows - 1) * ld + inner: the last row need not be padded.
   int st;
-  if ((st = split_fp32(piece, a, ah, al, (m - 1) * lda + k, stream)) != MFL_OK) return st;
-  if ((st = split_fp32(piece, b, bh, bl, (n - 1) * ldb + k, stream)) != MFL_OK) return st;
+  if ((st = split_fp32(piece, a, ah, al, (ra - 1) * lda + inner_a(m, k, order_a), stream)) != MFL_OK) return st;
+  if ((st = split_fp32(piece, b, bh, bl, (rb - 1) * ldb + inner_b(n, k, order_b), stream)) != MFL_OK) return st;
+  const bool akm = order_a == MFL_COL_MAJOR, bkm = order_b == MFL_ROW_MAJOR;
   hipStream_t s = (hipStream_t)stream;
   if (piece == MFL_BF16)
-    return dispatch_planes<MFL_BF16>(chains, lolo, ah, al, bh, bl, c, lda, ldb, ldc, (int)m, (int)n, (int)k,
-                                     accumulate, s);
-  return dispatch_planes<MFL_F16>(chains, lolo, ah, al, bh, bl, c, lda, ldb, ldc, (int)m, (int)n, (int)k, accumulate,
-                                  s);
+    return dispatch_planes_orders<MFL_BF16>(akm, bkm, chains, lolo, ah, al, bh, bl, c, lda, ldb, ldc, (int)m, (int)n,
+                                            (int)k, accumulate, s);
+  return dispatch_planes_orders<MFL_F16>(akm, bkm, chains, lolo, ah, al, bh, bl, c, lda, ldb, ldc, (int)m, (int)n,
+                                         (int)k, accumulate, s);
 }

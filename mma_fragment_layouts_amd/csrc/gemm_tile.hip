@@ -90,60 +90,6 @@ static int launch_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, f
 // scalar offsets.  Sixteen waves (four per SIMD, 64 x 64 outputs each) let one
 // wave's MFMAs run while another waits on LDS or on the barrier; at
 // 256 x 256 x 64 the fragment traffic (conflict free) stays below the MFMA time.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Direct-to-LDS loads of one operand's R x 64 slab per stage.
-//   K-contiguous (A row-major, B column-major): R rows of 64 K values, 128 bytes
-//     each, chunk XOR swz<64>(row); a load instruction fills 8 rows.
-//   k-major (A column-major, B row-major): the kmaj_chunk layout; a load
-//     instruction fills 64 consecutive chunks, 8 K rows x 128 contiguous bytes.
-// Load instruction i of wave w fills bytes (i*NW + w)*1024 .. +1024 of the slab.
-template <int SHAPE, int R, int NW, bool KMAJOR>
-struct DmaOperand {
-  static constexpr int INSTR = R / 8 / NW;
-  static_assert(INSTR * 8 * NW == R, "slab must split into whole wave loads");
-  // K-contiguous: every load instruction of a wave starts at the same row mod 16,
-  // so the swizzle — and the per-lane offset — is the same for all of them.
-  static_assert(KMAJOR || (NW * 8) % 16 == 0, "per-lane swizzle must be load-invariant");
-  static_assert(!KMAJOR || ((NW & (NW - 1)) == 0 && (R == 128 || R == 256)), "k-major slab shape");
-  rsrc_t rs;
-  uint32_t voff, ld2;
-
-  // X: the operand; r0: first M (or N) index of the tile; ld: leading dimension.
-  __device__ __forceinline__ DmaOperand(const uint16_t* X, uint32_t ld, int r0, int K, int wave, int lane) {
-    ld2 = ld * 2u;
-    if constexpr (KMAJOR) {
-      rs = make_rsrc(X + r0, (uint32_t)K * ld2);
-      // chunk (i*NW + wave)*64 + lane: the bits of i, wave and lane are disjoint
-      // and the layout permutes bits, so their (k, r) offsets add.
-      int k = 0, r = 0;
-      kmaj_coords<SHAPE>(wave * 64 + lane, &k, &r);
-      voff = (uint32_t)k * ld2 + (uint32_t)r * 2u;
-    } else {
-      rs = make_rsrc(X + (int64_t)r0 * ld, (uint32_t)R * ld2);
-      const int row = wave * 8 + (lane >> 3);
-      voff = (uint32_t)row * ld2 + (uint32_t)(((lane & 7) ^ swz<64>(row)) << 4);
-    }
-  }
-  __device__ __forceinline__ void issue(uint16_t* slab, int wave, int k0) const {
-#pragma unroll
-    for (int i = 0; i < INSTR; ++i) {
-      uint32_t soff;
-      if constexpr (KMAJOR) {
-        int ki = 0, ri = 0;
-        kmaj_coords<SHAPE>(i * NW * 64, &ki, &ri);
-        soff = (uint32_t)(ki + k0) * ld2 + (uint32_t)ri * 2u;
-      } else {
-        soff = (uint32_t)(i * NW * 8) * ld2 + (uint32_t)k0 * 2u;
-      }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(slab + (i * NW + wave) * 512), 16, voff, soff, 0, 0);
-    }
-  }
-};
-
 // STAGES-deep ring of LDS stages: stage kt+STAGES-1 is requested while stage kt
 // feeds the MFMAs.  One barrier per K step both publishes stage kt (every
 // wave's loads for it have landed) and retires stage kt-1, whose buffer the
@@ -166,8 +112,8 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
   constexpr int LOADS = DA::INSTR + DB::INSTR;
   static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "vmcnt range");
   using Acc = typename Shape<SHAPE>::Acc;
-  using RA = std::conditional_t<AKM, KmFrag<SHAPE>, FragOffsets<SHAPE, BK>>;
-  using RB = std::conditional_t<BKM, KmFrag<SHAPE>, FragOffsets<SHAPE, BK>>;
+  using RA = std::conditional_t<AKM, KmFrag<SHAPE, BM, WM, TM>, FragOffsets<SHAPE, BK>>;
+  using RB = std::conditional_t<BKM, KmFrag<SHAPE, BN, WN, TN>, FragOffsets<SHAPE, BK>>;
 
   __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE];
 

@@ -316,12 +316,17 @@ def test_empty_problems_are_noops_without_a_device(lib):
 def test_split_planes_workspace_size(lib):
     R_, C_, S_, Rd = lib.ROW_MAJOR, lib.COL_MAJOR, lib.SPLIT, lib.ROUND
     al = lambda x: (x + 255) // 256 * 256
-    # applicable: four 16-bit planes, each operand rows x ld, 256-aligned
+    # applicable: four 16-bit planes in the operands' storage shapes (A: m rows
+    # row-major, k rows column-major; B: n rows column-major, k rows row-major)
+    # of ld elements each, 256-aligned
     assert lib.gemm_split_fp32_workspace_bytes(512, 384, 640, 648, R_, S_, 664, C_, S_, 384) == \
         2 * al(512 * 648 * 2) + 2 * al(384 * 664 * 2)
+    assert lib.gemm_split_fp32_workspace_bytes(512, 384, 640, 520, C_, S_, 392, R_, S_, 384) == \
+        2 * al(640 * 520 * 2) + 2 * al(640 * 392 * 2)
+    assert lib.gemm_split_fp32_workspace_bytes(512, 384, 640, 648, R_, S_, 392, R_, S_, 384) == \
+        2 * al(512 * 648 * 2) + 2 * al(640 * 392 * 2)
     # not applicable: no workspace (the split-on-load kernel runs)
     for args in [(512, 384, 640, 648, R_, Rd, 664, C_, S_, 384),   # A rounded
-                 (512, 384, 640, 648, C_, S_, 664, C_, S_, 384),   # A K-strided
                  (500, 384, 640, 648, R_, S_, 664, C_, S_, 384),   # M % 128
                  (512, 384, 600, 648, R_, S_, 664, C_, S_, 384),   # K % 64
                  (512, 384, 640, 644, R_, S_, 664, C_, S_, 384)]:  # lda % 8

@@ -123,23 +123,27 @@ def test_split_full_size_sampled():
 
 # ---- planes path (gemm_split_fp32_ws): operands split once into hi / lo planes
 
-def run_both(a, bt, chains, lolo, piece, accumulate=0, seed=0):
+def run_both(a, bt, chains, lolo, piece, accumulate=0, seed=0, oa=mfl.ROW_MAJOR, ob=mfl.COL_MAJOR):
     """The same product through gemm_split_fp32 (split on load) and
-    gemm_split_fp32_ws (planes); leading dimensions padded with NaN and
-    different for A and B; C preset to random values when accumulating."""
+    gemm_split_fp32_ws (planes), A (M x K) and B (K x N, given as bt = B^T)
+    stored in orders oa / ob; leading dimensions padded with NaN and different
+    for A and B; C preset to random values when accumulating."""
     m, k = a.shape
     n = bt.shape[0]
-    lda, ldb = k + (-k) % 8 + 8, k + (-k) % 8 + 24
-    da, db = dev32(padded(a, lda)), dev32(padded(bt, ldb))
-    wsb = mfl.gemm_split_fp32_workspace_bytes(m, n, k, lda, mfl.ROW_MAJOR, mfl.SPLIT, ldb, mfl.COL_MAJOR, mfl.SPLIT, n)
+    sa = a if oa == mfl.ROW_MAJOR else np.ascontiguousarray(a.T)     # storage rows x inner
+    sb = bt if ob == mfl.COL_MAJOR else np.ascontiguousarray(bt.T)
+    lda = sa.shape[1] + (-sa.shape[1]) % 8 + 8
+    ldb = sb.shape[1] + (-sb.shape[1]) % 8 + 24
+    da, db = dev32(padded(sa, lda)), dev32(padded(sb, ldb))
+    wsb = mfl.gemm_split_fp32_workspace_bytes(m, n, k, lda, oa, mfl.SPLIT, ldb, ob, mfl.SPLIT, n)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=device())
     c0 = np.random.default_rng(seed).standard_normal((m, n)).astype(np.float32) if accumulate else \
         np.full((m, n), np.nan, np.float32)
     c_load, c_planes = dev32(c0), dev32(c0)
-    mfl.gemm_split_fp32(DT[piece], m, n, k, da, lda, mfl.ROW_MAJOR, mfl.SPLIT, db, ldb, mfl.COL_MAJOR, mfl.SPLIT,
-                        chains, lolo, c_load, n, accumulate, stream())
-    mfl.gemm_split_fp32_ws(DT[piece], m, n, k, da, lda, mfl.ROW_MAJOR, mfl.SPLIT, db, ldb, mfl.COL_MAJOR, mfl.SPLIT,
-                           chains, lolo, c_planes, n, accumulate, ws, wsb, stream())
+    mfl.gemm_split_fp32(DT[piece], m, n, k, da, lda, oa, mfl.SPLIT, db, ldb, ob, mfl.SPLIT, chains, lolo, c_load, n,
+                        accumulate, stream())
+    mfl.gemm_split_fp32_ws(DT[piece], m, n, k, da, lda, oa, mfl.SPLIT, db, ldb, ob, mfl.SPLIT, chains, lolo, c_planes,
+                           n, accumulate, ws, wsb, stream())
     return host(c_load), host(c_planes), wsb
 
 
@@ -185,3 +189,30 @@ def test_split_planes_full_size_bit_identical():
         c_load, c_planes, wsb = run_both(a, bt, chains, 0, "bf16")
         assert wsb > 0
         assert np.array_equal(c_load.view(np.uint32), c_planes.view(np.uint32))
+
+
+# K-strided operands (A column-major, B row-major) take the planes path too:
+# their planes are staged k-major and read with the transpose read.  Same MFMAs
+# in the same order, so the result is still bit-identical to split on load.
+STRIDED = [(mfl.ROW_MAJOR, mfl.ROW_MAJOR), (mfl.COL_MAJOR, mfl.COL_MAJOR), (mfl.COL_MAJOR, mfl.ROW_MAJOR)]
+
+
+@pytest.mark.parametrize("orders", STRIDED)
+@pytest.mark.parametrize("piece,chains,lolo,accumulate", [("bf16", 3, 0, 0), ("f16", 1, 0, 1), ("bf16", 2, 1, 1)])
+def test_split_planes_k_strided_orders_bit_identical(orders, piece, chains, lolo, accumulate):
+    a, bt = inputs.gemm_split(384, 256, 640)
+    say("split planes orders", orders, piece, chains, lolo, accumulate)
+    c_load, c_planes, wsb = run_both(a, bt, chains, lolo, piece, accumulate, seed=7, oa=orders[0], ob=orders[1])
+    assert wsb > 0
+    assert not np.isnan(c_planes).any()
+    assert np.array_equal(c_load.view(np.uint32), c_planes.view(np.uint32))
+
+
+def test_split_planes_k_strided_against_oracle(medium):
+    """A column-major, B row-major, 512 x 384 x 2048: within the oracle bounds."""
+    a, bt, ref, exp3, _ = medium
+    say("split planes strided oracle")
+    _, c, wsb = run_both(a, bt, 3, 0, "bf16", oa=mfl.COL_MAJOR, ob=mfl.ROW_MAJOR)
+    assert wsb > 0
+    assert R.rel_error(c, ref) <= 5e-6
+    assert R.rel_error(c, exp3) <= 2e-6
