@@ -61,17 +61,27 @@ def best_of(fn, stream, warm=3, rounds=3, per=20):
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_4096_bf16_traffic.json")
 
 
+def source_digest(paths):
+    """sha256 of the given sources with C/C++ comments and whitespace removed, so
+    that edits of comments alone do not count as a kernel change."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for src in paths:
+        text = open(os.path.join(ROOT, src)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     record (scaled by a plain copy), or None when the kernel sources have changed
     since the counters were taken."""
-    import hashlib
     try:
         rec = json.load(open(TRAFFIC_RECORD))
-        h = hashlib.sha256()
-        for src in rec["sources"]:
-            h.update(open(os.path.join(ROOT, src), "rb").read())
-        if h.hexdigest() != rec["source_sha256"]:
+        if source_digest(rec["sources"]) != rec["source_digest"]:
             return None
         return int(rec["read_bytes"] + rec["write_bytes"])
     except Exception:

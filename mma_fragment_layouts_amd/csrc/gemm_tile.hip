@@ -81,15 +81,15 @@ static int launch_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, f
 
 // ---------------------------------------------------------------------------
 // Fast path: M % BM == 0, N % BN == 0, K % 64 == 0, either operand order.
-// Global -> LDS moves use the CDNA4 direct-to-LDS buffer load
-// (buffer_load_dwordx4 ... lds): one wave instruction writes 64 x 16 bytes to
-// consecutive LDS addresses, with no staging registers.  The swizzle is applied
-// on the source side: the lane that lands in physical chunk p of a tile row
-// fetches logical chunk p ^ swizzle(row).  Per-lane state is one 32-bit offset
-// per operand; the row step of each load instruction and the K step are uniform
-// scalar offsets.  Sixteen waves (four per SIMD, 64 x 64 outputs each) let one
-// wave's MFMAs run while another waits on LDS or on the barrier; at
-// 256 x 256 x 64 the fragment traffic (conflict free) stays below the MFMA time.
+// Global -> LDS moves use the CDNA4 direct-to-LDS buffer load (DmaOperand: one
+// wave instruction writes 64 x 16 bytes to consecutive LDS addresses, with no
+// staging registers, the layout applied on the source side).  Per-lane state is
+// one 32-bit offset per operand; the row step of each load instruction and the
+// K step are uniform scalar offsets.  Sixteen waves (four per SIMD, 64 x 64
+// outputs each) let one wave's MFMAs run while another waits on LDS or on the
+// barrier; at 256 x 256 x 64 the fragment traffic (conflict free) stays below
+// the MFMA time.
+//
 // STAGES-deep ring of LDS stages: stage kt+STAGES-1 is requested while stage kt
 // feeds the MFMAs.  One barrier per K step both publishes stage kt (every
 // wave's loads for it have landed) and retires stage kt-1, whose buffer the
