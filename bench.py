@@ -8,14 +8,19 @@ accumulation and fp32 output (ldc = 4096).  One step = one gemm_tile_mma call
 output element).  Operands are rounded to bf16 by the library before timing,
 as the workload specifies bf16 inputs.
 
+Timing: prewarm_ms (default 100) of untimed back-to-back steps — the GPU takes
+about 200 launches to settle after a cold start — then W untimed warm-up steps,
+then exactly K timed steps between two synchronisations.
+
 Prints ONE JSON line with the metric, a roofline object for the GEMM kernel
 (flops per launch / mean launch time from HIP events on the launch stream),
 the CPU oracle's throughput on the host cores, and per-workload figures for
-the other four workloads (single 256^3 GEMM, block-repeat tiles, split fp32
-GEMM with 1/2/3 chains, attention pair), each timed as 3 warm-up launches
-then the best of 3 rounds of 20 back-to-back launches.
+the other workloads (single 256^3 GEMM, the 4096^3 GEMM in every operand
+order, block-repeat tiles, split fp32 GEMM with 1/2/3 chains, attention pair),
+each timed as 3 warm-up launches (and at least 30 ms of settling launches) then
+the best of 3 rounds of 20 back-to-back launches.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-ms T] [--no-extra]
 """
 from __future__ import annotations
 
@@ -50,11 +55,25 @@ def event_time_ms(fn, n, stream):
     return start.elapsed_time(end)
 
 
-def best_of(fn, stream, warm=3, rounds=3, per=20):
+def settle(fn, ms):
+    """Launch fn back to back, untimed, for at least ms milliseconds: after host
+    work the GPU has idled and its clocks take tens of milliseconds of load to
+    settle again."""
+    import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+
+
+def best_of(fn, stream, warm=3, rounds=3, per=20, settle_ms=30.0):
     """Timing protocol of the Warp spike: 3 warm-up launches, then the best of
-    3 rounds of 20 back-to-back launches; returns ms per launch."""
+    3 rounds of 20 back-to-back launches; returns ms per launch.  The warm-up
+    also runs for at least settle_ms (clock settling)."""
     for _ in range(warm):
         fn()
+    settle(fn, settle_ms)
     return min(event_time_ms(fn, per, stream) for _ in range(rounds)) / per
 
 
@@ -308,6 +327,8 @@ def main():
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--extra", default=",".join(EXTRA),
                    help="comma list of the other workloads to run (" + ", ".join(EXTRA) + ")")
+    p.add_argument("--prewarm-ms", type=float, default=100.0,
+                   help="untimed back-to-back GEMM launches before the warm-up steps, in ms (clock settling)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-clock", action="store_true", help="skip the SCLK reading under load")
     p.add_argument("--copy-calibration", action="store_true",
@@ -345,6 +366,11 @@ def main():
         mfl.gemm_tile_mma_shape(args.shape, mfl.BF16, M, N, K, da, LD, mfl.ROW_MAJOR, db, LD, mfl.COL_MAJOR, c, N, 0,
                                 stream)
 
+    # The GPU takes about 200 back-to-back launches (~25 ms) to settle after a
+    # cold start (launches 100-199 measured 4-7 % slower than the steady state);
+    # run the same step untimed for prewarm_ms before the warm-up steps.
+    log("prewarm", args.prewarm_ms, "ms")
+    settle(step, args.prewarm_ms)
     log("warmup", args.warmup)
     for _ in range(args.warmup):
         step()
@@ -383,7 +409,8 @@ def main():
         "config": {"workload": "dense GEMM M=N=K=4096, bf16 A row-major / B col-major, lda=ldb=4160 (NaN pad), "
                                "fp32 accumulate, fp32 C ldc=4096",
                    "m": M, "n": N, "k": K, "lda": LD, "ldb": LD, "ldc": N,
-                   "mfma": "16x16x32" if args.shape == 0 else "32x32x16", "tile": "256x256x64, 16 waves (64x64 each)"},
+                   "mfma": "16x16x32" if args.shape == 0 else "32x32x16", "tile": "256x256x64, 16 waves (64x64 each)",
+                   "prewarm_ms": args.prewarm_ms},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
