@@ -1,5 +1,5 @@
 // Kernels of the fused split-precision attention (design notes in
-// attention_fused.hpp): preparation of K and V^T in fp16, the fused per-slice
+// attention_fused.hpp): preparation of K and V in fp16, the fused per-slice
 // kernel, and the fixed-order combine of the key slices.
 #include "attention_fused.hpp"
 
@@ -23,28 +23,27 @@ __device__ __forceinline__ Split2 split2(float a, float b) {
   return {__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};
 }
 
-// One workgroup per 32-key block (256 threads):
-//   K (nk x 128 fp32) -> K16 (nk x 128 fp16, round to nearest even);
-//   V (nk x 128 fp32) -> V16^T (128 x nk fp16), the keys of each 32-key block
-//   stored at vt_key_pos(r).
-// K: thread t converts 16 consecutive values (four 16-byte loads, two 16-byte
-// stores).  V: thread (pair, oct) gathers dims 2 pair, 2 pair + 1 of the keys
-// at storage positions 8 oct .. 8 oct + 7 (8-byte loads: a wave's 64 lanes read
-// one whole 512-byte key row per load) and stores 16 bytes per dim.
-// SKV: K and V are split as well — K16 and V16^T hold the hi parts and Kl and
-// Vtl (same layouts) the lo parts, lo = RNE16(x - hi).
+// Elementwise preparation of K and V (both nk x 128 fp32, key-major) into
+// K16 and V16 (fp16, round to nearest even, same layout); with SKV also the lo
+// planes Kl and Vl, lo = RNE16(x - hi).  Thread t of workgroup b converts the
+// 16 consecutive values 16*(256*b + t) .. +15 of each operand (four 16-byte
+// loads, two 16-byte stores per plane); n16 = nk * 128 / 16 threads in all.
 template <bool SKV>
 __global__ __launch_bounds__(256) void attn_prep(const float* __restrict__ K, const float* __restrict__ V,
-                                                 uint16_t* __restrict__ Kq, uint16_t* __restrict__ Vt,
-                                                 uint16_t* __restrict__ Kl, uint16_t* __restrict__ Vtl, int nk) {
-  const int blk = blockIdx.x, t = threadIdx.x;
-  const int64_t base = (int64_t)blk * 32 * kAttnD;
-  {
-    const int64_t idx = base + (int64_t)t * 16;
+                                                 uint16_t* __restrict__ Kq, uint16_t* __restrict__ Vq,
+                                                 uint16_t* __restrict__ Kl, uint16_t* __restrict__ Vl, int64_t n16) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n16) return;
+  const int64_t idx = t * 16;
+#pragma unroll
+  for (int op = 0; op < 2; ++op) {
+    const float* X = op ? V : K;
+    uint16_t* H = op ? Vq : Kq;
+    uint16_t* L = op ? Vl : Kl;
     uint32_t wh[8], wl[8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(K + idx + 4 * q);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(X + idx + 4 * q);
       const Split2 a = split2(x[0], x[1]), b = split2(x[2], x[3]);
       wh[2 * q] = a.hi;
       wh[2 * q + 1] = b.hi;
@@ -53,40 +52,15 @@ __global__ __launch_bounds__(256) void attn_prep(const float* __restrict__ K, co
     }
     u32x4 o;
     __builtin_memcpy(&o, wh, 16);
-    *reinterpret_cast<u32x4*>(Kq + idx) = o;
+    *reinterpret_cast<u32x4*>(H + idx) = o;
     __builtin_memcpy(&o, wh + 4, 16);
-    *reinterpret_cast<u32x4*>(Kq + idx + 8) = o;
+    *reinterpret_cast<u32x4*>(H + idx + 8) = o;
     if constexpr (SKV) {
       __builtin_memcpy(&o, wl, 16);
-      *reinterpret_cast<u32x4*>(Kl + idx) = o;
+      *reinterpret_cast<u32x4*>(L + idx) = o;
       __builtin_memcpy(&o, wl + 4, 16);
-      *reinterpret_cast<u32x4*>(Kl + idx + 8) = o;
+      *reinterpret_cast<u32x4*>(L + idx + 8) = o;
     }
-  }
-  const int pair = t & 63, oct = t >> 6;  // dims 2 pair, 2 pair + 1; positions 8 oct ..
-  uint16_t h0[8], h1[8], l0[8], l1[8];
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const f32x2 x =
-        *reinterpret_cast<const f32x2*>(V + base + (int64_t)vt_pos_key(8 * oct + p) * kAttnD + 2 * pair);
-    h0[p] = to16<MFL_F16>(x.x);
-    h1[p] = to16<MFL_F16>(x.y);
-    if constexpr (SKV) {
-      l0[p] = to16<MFL_F16>(x.x - from16<MFL_F16>(h0[p]));
-      l1[p] = to16<MFL_F16>(x.y - from16<MFL_F16>(h1[p]));
-    }
-  }
-  const int64_t d0 = (int64_t)(2 * pair) * nk + (int64_t)blk * 32 + 8 * oct;
-  u32x4 o;
-  __builtin_memcpy(&o, h0, 16);
-  *reinterpret_cast<u32x4*>(Vt + d0) = o;
-  __builtin_memcpy(&o, h1, 16);
-  *reinterpret_cast<u32x4*>(Vt + d0 + nk) = o;
-  if constexpr (SKV) {
-    __builtin_memcpy(&o, l0, 16);
-    *reinterpret_cast<u32x4*>(Vtl + d0) = o;
-    __builtin_memcpy(&o, l1, 16);
-    *reinterpret_cast<u32x4*>(Vtl + d0 + nk) = o;
   }
 }
 
@@ -124,22 +98,22 @@ __device__ __forceinline__ void attn_block_of(int b, int nwg, int qblocks, int x
 // in real arithmetic.
 //
 //
-// SKV: K and V are split too (hi planes Kq / Vt, lo planes Kl / Vtl).  A stage
+// SKV: K and V are split too (hi planes Kq / Vq, lo planes Kl / Vl).  A stage
 // then holds the lo tiles after the hi ones, and each GEMM adds the third
 // product into the correction chain: S = Kh Qh | (Kh Ql + Kl Qh), O += Vh Ph |
 // (Vh Pl + Vl Ph).
 template <int CHAINS, int STAGES, bool SKV>
 __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict__ Q, const uint16_t* __restrict__ Kq,
-                                                         const uint16_t* __restrict__ Vt,
+                                                         const uint16_t* __restrict__ Vq,
                                                          const uint16_t* __restrict__ Kl,
-                                                         const uint16_t* __restrict__ Vtl, float* __restrict__ Opart,
+                                                         const uint16_t* __restrict__ Vl, float* __restrict__ Opart,
                                                          float* __restrict__ Mpart, float* __restrict__ Lpart, int nq,
                                                          int nk, int keys_per_split, int qblocks, int xcd_map) {
   static_assert(kAttnQ == 128 && kAttnKV == 64 && kAttnD == 128, "tiling below assumes 128 x 64 x 128");
   static_assert(STAGES >= 2, "at least double buffering");
-  constexpr int BK = 64;                    // LDS tile depth (dims for K16, keys for V16^T)
+  constexpr int BK = 64;                    // LDS tile depth of the K16 halves (dims)
   constexpr int KT = kAttnKV * BK;          // one K16 half tile: 64 keys x 64 dims
-  constexpr int HALF = 2 * KT + kAttnD * kAttnKV;  // K16 halves + V16^T tile (elements)
+  constexpr int HALF = 2 * KT + kAttnD * kAttnKV;  // K16 halves + k-major V16 tile (elements)
   constexpr int STAGE = SKV ? 2 * HALF : HALF;     // hi tiles, then (SKV) lo tiles
   constexpr int NW = 8;                     // waves per workgroup, 16 queries each
   constexpr int LOADS = 32 / NW;            // 1 KiB wave loads per stage per wave
@@ -173,27 +147,32 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
     }
   }
 
-  // Stage fill: 32 wave loads of 1 KiB (8 rows of 128 bytes); this wave issues
-  // blocks b = wave + NW*i.  Blocks 0-15: K16 half b/8, key rows 8*(b%8)..;
-  // blocks 16-31: V16^T dim rows 8*(b-16)...  Physical chunk lane%8 of row
-  // 8*blk + lane/8 receives logical chunk (lane%8) ^ swz(row).
+  // Stage fill: 32 wave loads of 1 KiB; this wave issues blocks b = wave + NW*i.
+  // Blocks 0-15: K16 half b/8, key rows 8*(b%8) .. +7 (128 bytes each); physical
+  // chunk lane%8 of row 8*blk + lane/8 receives logical chunk (lane%8) ^ swz(row).
+  // Blocks 16-31: the V16 chunk as a k-major tile (64 key rows x 128 dims, the
+  // kmaj_chunk layout of the 16x16x32 instruction), chunk 64*(b-16) + lane; its
+  // K row p holds key 32*(p/32) + vt_pos_key(p%32), so that GEMM2's transpose
+  // reads hand every lane the keys its P~ fragment holds.
   const rsrc_t rk = make_rsrc(Kq, (uint32_t)((int64_t)nk * kAttnD * 2));
-  const rsrc_t rv = make_rsrc(Vt, (uint32_t)((int64_t)nk * kAttnD * 2));
+  const rsrc_t rv = make_rsrc(Vq, (uint32_t)((int64_t)nk * kAttnD * 2));
   const rsrc_t rkl = make_rsrc(SKV ? Kl : Kq, (uint32_t)((int64_t)nk * kAttnD * 2));
-  const rsrc_t rvl = make_rsrc(SKV ? Vtl : Vt, (uint32_t)((int64_t)nk * kAttnD * 2));
+  const rsrc_t rvl = make_rsrc(SKV ? Vl : Vq, (uint32_t)((int64_t)nk * kAttnD * 2));
   uint32_t voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int b = wave + NW * i;  // wave-uniform
-    const int blk = b < 16 ? (b & 7) : b - 16;
-    const int row = 8 * blk + (lane >> 3);
-    const int lch = (lane & 7) ^ swz<BK>(row);
-    if (b < 16)
+    if (b < 16) {
+      const int row = 8 * (b & 7) + (lane >> 3);
+      const int lch = (lane & 7) ^ swz<BK>(row);
       voff[i] = (uint32_t)(row * kAttnD + 64 * (b >> 3) + lch * 8) * 2u;
-    else
-      voff[i] = (uint32_t)(row * nk + lch * 8) * 2u;
+    } else {
+      int p = 0, d = 0;
+      kmaj_coords<0>(64 * (b - 16) + lane, &p, &d);
+      voff[i] = (uint32_t)((32 * (p >> 5) + vt_pos_key(p & 31)) * kAttnD + d) * 2u;
+    }
   }
-  // With 8 waves, wave loads 0-1 (b = wave, wave + 8) fill K16 and 2-3 fill V16^T.
+  // With 8 waves, wave loads 0-1 (b = wave, wave + 8) fill K16 and 2-3 fill V16.
   static_assert(NW == 8 && LOADS == 4, "K16 / V16^T split of the wave loads assumes 8 waves");
   auto issue = [&](int chunk) {
     const uint32_t key0 = (uint32_t)(kbeg + chunk * kAttnKV);
@@ -209,13 +188,14 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (lds_ptr_t)(base + i * KT + wave * 8 * BK), 16, voff[i],
                                                    key0 * kAttnD * 2u, 0, 0);
         else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs, (lds_ptr_t)(base + 2 * KT + (b - 16) * 8 * BK), 16, voff[i],
-                                                   key0 * 2u, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs, (lds_ptr_t)(base + 2 * KT + (b - 16) * 512), 16, voff[i],
+                                                   key0 * kAttnD * 2u, 0, 0);
       }
     }
   };
 
-  const FragOffsets<0, BK> fo(0, lane);  // lane row lr, chunk 4*kk + g
+  const FragOffsets<0, BK> fo(0, lane);  // K16 reads: lane row lr, chunk 4*kk + g
+  const KmFrag<0, kAttnD, kAttnD, 8> fv(0, lane);  // V16 reads: 8 dim tiles, transpose reads
 
   // GEMM1 of one chunk: S^T (64 keys x 16 queries) = K16 . (log2e Q)^T, hi and
   // lo products in chains sh / sl (CHAINS == 2) or both in sh.
@@ -296,18 +276,20 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
       }
   };
 
-  // GEMM2 of one chunk: O^T (128 dims x 16 queries) += V16^T . P~^T.
+  // GEMM2 of one chunk: O^T (128 dims x 16 queries) += V16^T . P~^T, the V16^T
+  // fragments (dims 16i.., K positions 32t + 8g + ..) read from the k-major V16
+  // tile with the transpose read.
   auto gemm2 = [&](int chunk, const u32x4 (&ph)[2], const u32x4 (&pl)[2]) {
     const uint16_t* sv = lds + (chunk % STAGES) * STAGE + 2 * KT;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const u32x4 a = lds_read16(sv, fo.off[t] + i * 16 * BK);
+        const u32x4 a = frag_read(sv, fv, t, i);
         oh[i] = mfma<0, MFL_F16>(a, ph[t], oh[i]);
         f32x4& corr = CHAINS == 2 ? ol[i] : oh[i];
         corr = mfma<0, MFL_F16>(a, pl[t], corr);
-        if constexpr (SKV) corr = mfma<0, MFL_F16>(lds_read16(sv + HALF, fo.off[t] + i * 16 * BK), ph[t], corr);
+        if constexpr (SKV) corr = mfma<0, MFL_F16>(frag_read(sv + HALF, fv, t, i), ph[t], corr);
       }
   };
 
@@ -406,14 +388,14 @@ int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, co
   char* w = (char*)workspace;
   uint16_t* kq = (uint16_t*)w;
   w += al(nk * kAttnD * 2);
-  uint16_t* vt = (uint16_t*)w;
+  uint16_t* vq = (uint16_t*)w;
   w += al(nk * kAttnD * 2);
   uint16_t* kl = nullptr;
-  uint16_t* vtl = nullptr;
+  uint16_t* vl = nullptr;
   if (skv) {
     kl = (uint16_t*)w;
     w += al(nk * kAttnD * 2);
-    vtl = (uint16_t*)w;
+    vl = (uint16_t*)w;
     w += al(nk * kAttnD * 2);
   }
   float* op = (float*)w;
@@ -421,11 +403,12 @@ int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, co
   float* mp = (float*)w;
   w += al(splits * nq * 4);
   float* lp = (float*)w;
-  const dim3 pgrid((unsigned)(nk / 32)), pblock(256);
+  const int64_t n16 = nk * kAttnD / 16;  // 16-value groups per operand
+  const dim3 pgrid((unsigned)((n16 + 255) / 256)), pblock(256);
   if (skv)
-    hipLaunchKernelGGL(attn_prep<true>, pgrid, pblock, 0, st, k, v, kq, vt, kl, vtl, (int)nk);
+    hipLaunchKernelGGL(attn_prep<true>, pgrid, pblock, 0, st, k, v, kq, vq, kl, vl, n16);
   else
-    hipLaunchKernelGGL(attn_prep<false>, pgrid, pblock, 0, st, k, v, kq, vt, kl, vtl, (int)nk);
+    hipLaunchKernelGGL(attn_prep<false>, pgrid, pblock, 0, st, k, v, kq, vq, kl, vl, n16);
   const int qblocks = (int)(nq / kAttnQ);
   const int nwg = qblocks * (int)splits;
   const int xcd_map = nwg % 8 == 0;
@@ -434,7 +417,7 @@ int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, co
   // two LDS stages: measured as fast as three, and a third adds nothing at
   // one workgroup per CU
 #define MFL_ATTN_LAUNCH(CH, SK)                                                                                      \
-  hipLaunchKernelGGL((attn_fused_kernel<CH, 2, SK>), grid, block, 0, st, q, kq, vt, kl, vtl, op, mp, lp, (int)nq,      \
+  hipLaunchKernelGGL((attn_fused_kernel<CH, 2, SK>), grid, block, 0, st, q, kq, vq, kl, vl, op, mp, lp, (int)nq,      \
                      (int)nk, kps, qblocks, xcd_map)
   if (skv) {
     if (chains == 2)

@@ -22,10 +22,11 @@
 // Layout trick: the S^T accumulator gives lane l (query l mod 16, group
 // g = l div 16) the keys 16*t' + 4g + j of each 16-key tile t'.  For GEMM2 the
 // lane's 8 K positions 8g..8g+7 of 32-key block t are taken to be keys
-// 32t + 4g + j (from tile 2t) and 32t + 16 + 4g + j (from tile 2t + 1); the
-// preparation pass stores V^T with the keys of every 32-key block permuted so
-// that exactly those 8 keys are contiguous — then the V^T fragment is one
-// 16-byte read like any other.
+// 32t + 4g + j (from tile 2t) and 32t + 16 + 4g + j (from tile 2t + 1).  V stays
+// key-major in HBM (K16 and V16 are plain fp16 copies); the direct-to-LDS loads
+// put key 32t + vt_pos_key(p) into K row 32t + p of a k-major V16 tile, and the
+// gfx950 transpose read then hands every lane exactly those 8 keys for its 16
+// dims.
 #pragma once
 #include "gemm_core.hpp"
 
@@ -41,7 +42,7 @@ constexpr float kAttnSlack = 8.f;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 
-// Storage position of key r (0..31) inside its 32-key block of V^T.
+// K row of key r (0..31) inside its 32-key block of the k-major V16 tile.
 MFL_HD constexpr int vt_key_pos(int r) { return 8 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3); }
 
 constexpr bool vt_perm_is_bijection() {

@@ -349,7 +349,7 @@ def test_attention_workspace_size(lib):
     b = lib.attention_workspace_bytes(2048, 32768, 128, 0)
     assert b >= 2048 * 32768 * 4 + 2 * 2048 * 4 + 2048 * 128 * 4
     f = lib.attention_workspace_bytes(2048, 32768, 128, 1)
-    # fp16 K and V^T plus per-slice partial O, m, l: far below the materialised scores
+    # fp16 K and V plus per-slice partial O, m, l: far below the materialised scores
     assert 2 * 32768 * 128 * 2 < f < b // 4
     with pytest.raises(lib.MflError):
         lib.attention_workspace_bytes(2048, 32768, 96, 1)
@@ -361,7 +361,7 @@ def test_attention_workspace_size(lib):
         assert e.value.status == lib.EUNSUPPORTED
     assert lib.attention_workspace_bytes(128, 1 << 24, 128, 0) > 0
     skv = lib.attention_workspace_bytes(2048, 32768, 128, 2)
-    assert skv == f + 2 * 32768 * 128 * 2      # K and V^T lo planes on top
+    assert skv == f + 2 * 32768 * 128 * 2      # K and V lo planes on top
     with pytest.raises(lib.MflError):
         lib.attention_workspace_bytes(2048, 32768, 128, 5)
     with pytest.raises(lib.MflError):
