@@ -6,11 +6,6 @@
 namespace mfl {
 namespace attn_detail {
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // Packed hi/lo split of two fp32 values into fp16 pairs: hi = RNE16(x),
 // lo = RNE16(x - hi), with x - hi exact in fp32.
 struct Split2 {
@@ -300,9 +295,9 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
     if (s < nchunks) issue(s);
   for (int c = 0; c < nchunks; ++c) {
     if (c + STAGES - 2 < nchunks)
-      wait_vm<(STAGES - 2) * LOADS>();
+      wait_vmcnt<(STAGES - 2) * LOADS>();
     else
-      wait_vm<0>();
+      wait_vmcnt<0>();
     __syncthreads();
     if (c + STAGES - 1 < nchunks) issue(c + STAGES - 1);
     f32x4 sh[4], sl[4];
