@@ -192,12 +192,15 @@ MFL_API int split_fp32(int dtype, const float *x, void *hi, void *lo, int64_t n,
  * accumulation kept in registers across the whole K loop; each output tile is
  * stored once through the accumulator layout (Warp issue #1965, "Proposed
  * change" and "Design consequences").  Operand orders are free.  The fast path
- * takes M and N multiples of 128 (of 64 when A is row-major and B
- * column-major), K a multiple of 64, and buffers within 4 GiB (256 rows of
+ * takes K a multiple of 64, M a multiple of 8 when A is column-major and N a
+ * multiple of 8 when B is row-major, and buffers within 4 GiB (256 rows of
  * lda / ldb / ldc; K rows of lda for column-major A, of ldb for row-major B);
- * a column-major A or row-major B is staged K-major in LDS and read with the
+ * M and N need not be tile multiples (the last tiles are clipped, and nothing
+ * outside the m x n block of C, padding included, is written).  A
+ * column-major A or row-major B is staged K-major in LDS and read with the
  * gfx950 transpose read, with results bit-identical to the K-contiguous
- * orders.  Other sizes take the generic path. */
+ * orders.  Other sizes take the generic path.  Reads never go past the
+ * minimum storage of an operand, (rows - 1) * ld + the inner extent. */
 MFL_API int gemm_tile_mma(int dtype, int64_t m, int64_t n, int64_t k,
                   const void *a, int64_t lda, int order_a,
                   const void *b, int64_t ldb, int order_b,

@@ -202,14 +202,24 @@ __device__ __forceinline__ u32x4 lds_read_tr(const uint16_t* lds, int elem_off, 
 
 __device__ __forceinline__ u32x4 gload16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// Zero the 16-bit lanes of a chunk whose K index (k_first + e) is >= k_end.
-__device__ __forceinline__ u32x4 mask_tail(u32x4 v, int k_first, int k_end) {
+// The first n (may be <= 0 or >= 8) of 8 consecutive 16-bit values, read one
+// by one, the rest zero: no read at or past p + n.
+__device__ __forceinline__ u32x4 gload_partial(const uint16_t* p, int n) {
   uint16_t h[8];
-  __builtin_memcpy(h, &v, 16);
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (k_first + e >= k_end) h[e] = 0;
+  for (int e = 0; e < 8; ++e) h[e] = e < n ? p[e] : (uint16_t)0;
+  u32x4 v;
   __builtin_memcpy(&v, h, 16);
+  return v;
+}
+
+// The first n (may be <= 0 or >= 4) of 4 consecutive fp32 values, read one by
+// one, the rest zero: no read at or past p + n.
+__device__ __forceinline__ f32x4 gload4_partial(const float* p, int n) {
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (e < n) v[e] = p[e];
   return v;
 }
 

@@ -21,8 +21,10 @@ namespace mfl {
 //   KC = false: element (r, k) is at base[(k0 + k)*ld + r0 + r] (K strided);
 //               16-byte loads along R, scattered 2-byte LDS writes.
 // EDGE enables masking: K positions >= k_total are zero (in both operands, so a
-// NaN in padding never meets a zero), R positions past rows_total are read from
-// in-bounds storage but never stored by the epilogue.
+// NaN in padding never meets a zero), R positions past rows_total are zero (KC =
+// false) or repeat the last row (KC = true) and are never stored by the
+// epilogue.  A chunk that straddles the edge is read element by element, so no
+// read leaves the operand's storage ((rows - 1) * ld + inner extent).
 template <int R, int BK, int NT, bool KC, bool EDGE>
 struct TileLoader {
   static constexpr int CHUNKS = R * BK / 8;
@@ -43,18 +45,18 @@ struct TileLoader {
           gr = min(gr, rows_total - 1);
           if (kf + 8 <= k_total)
             reg[i] = gload16(base + (int64_t)gr * ld + kf);
-          else if (kf < k_total)
-            reg[i] = mask_tail(gload16(base + (int64_t)gr * ld + kf), kf, k_total);
           else
-            reg[i] = u32x4{0, 0, 0, 0};
+            reg[i] = gload_partial(base + (int64_t)gr * ld + kf, k_total - kf);
         } else {
           reg[i] = gload16(base + (int64_t)gr * ld + kf);
         }
       } else {
         const int k = idx / (R / 8), rc = idx % (R / 8);
         const int gk = k0 + k, gr = r0 + rc * 8;
-        if (!EDGE || (gk < k_total && gr < rows_total))
+        if (!EDGE || (gk < k_total && gr + 8 <= rows_total))
           reg[i] = gload16(base + (int64_t)gk * ld + gr);
+        else if (gk < k_total)
+          reg[i] = gload_partial(base + (int64_t)gk * ld + gr, rows_total - gr);
         else
           reg[i] = u32x4{0, 0, 0, 0};
       }
@@ -225,7 +227,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 //   k-major (A column-major, B row-major): the kmaj_chunk layout; a load
 //     instruction fills 64 consecutive chunks, 8 K rows x 128 contiguous bytes.
 // Load instruction i of wave w fills bytes (i*NW + w)*1024 .. +1024 of the slab.
-template <int SHAPE, int R, int NW, bool KMAJOR>
+// EDGE: only `valid` (< R) rows / columns of the tile exist.  The buffer extent
+// then ends at the last valid element — K-contiguous: after `valid` rows;
+// k-major: at column `valid` of the last K row — and the loads return zeros
+// from there on (the hardware checks every dword against the extent); columns
+// past `valid` in the earlier K rows of a k-major tile read neighbouring
+// storage.  Either way they only feed outputs that are never stored.
+template <int SHAPE, int R, int NW, bool KMAJOR, bool EDGE = false>
 struct DmaOperand {
   static constexpr int INSTR = R / 8 / NW;
   static_assert(INSTR * 8 * NW == R, "slab must split into whole wave loads");
@@ -236,18 +244,21 @@ struct DmaOperand {
   rsrc_t rs;
   uint32_t voff, ld2;
 
-  // X: the operand; r0: first M (or N) index of the tile; ld: leading dimension.
-  __device__ __forceinline__ DmaOperand(const uint16_t* X, uint32_t ld, int r0, int K, int wave, int lane) {
+  // X: the operand; r0: first M (or N) index of the tile; ld: leading dimension;
+  // valid: M (or N) - r0, used when EDGE.
+  __device__ __forceinline__ DmaOperand(const uint16_t* X, uint32_t ld, int r0, int K, int wave, int lane,
+                                        int valid = R) {
     ld2 = ld * 2u;
+    const uint32_t v = EDGE ? (uint32_t)min(valid, R) : (uint32_t)R;
     if constexpr (KMAJOR) {
-      rs = make_rsrc(X + r0, (uint32_t)K * ld2);
+      rs = make_rsrc(X + r0, EDGE ? ((uint32_t)(K - 1) * ld + v) * 2u : (uint32_t)K * ld2);
       // chunk (i*NW + wave)*64 + lane: the bits of i, wave and lane are disjoint
       // and the layout permutes bits, so their (k, r) offsets add.
       int k = 0, r = 0;
       kmaj_coords<SHAPE>(wave * 64 + lane, &k, &r);
       voff = (uint32_t)k * ld2 + (uint32_t)r * 2u;
     } else {
-      rs = make_rsrc(X + (int64_t)r0 * ld, (uint32_t)R * ld2);
+      rs = make_rsrc(X + (int64_t)r0 * ld, v * ld2);
       const int row = wave * 8 + (lane >> 3);
       voff = (uint32_t)row * ld2 + (uint32_t)(((lane & 7) ^ swz<64>(row)) << 4);
     }
@@ -318,9 +329,11 @@ static_assert(acc_rows_separable(kAcc16x16x32) && acc_rows_separable(kAcc32x32x1
 
 // Epilogue through a buffer resource whose base is the wave tile's origin in C:
 // one 32-bit per-lane offset, uniform row offsets from the j digits.
-template <int SHAPE, int TM, int TN, bool ACCUM>
+// EDGE: columns from ncols on (relative to the origin) are not stored; rows past
+// the buffer's extent are dropped by the hardware.
+template <int SHAPE, int TM, int TN, bool ACCUM, bool EDGE = false>
 __device__ __forceinline__ void store_acc_rsrc(rsrc_t c, uint32_t ldc, int lane,
-                                               const typename Shape<SHAPE>::Acc (&acc)[TM][TN]) {
+                                               const typename Shape<SHAPE>::Acc (&acc)[TM][TN], int ncols = 0) {
   constexpr AccLayout L = acc_layout(SHAPE);
   constexpr int MN = Shape<SHAPE>::MN, J = Shape<SHAPE>::J;
   const uint32_t voff = ((uint32_t)acc_row(L, lane, 0) * ldc + (uint32_t)acc_col(L, lane, 0)) * 4u;
@@ -331,6 +344,8 @@ __device__ __forceinline__ void store_acc_rsrc(rsrc_t c, uint32_t ldc, int lane,
       const uint32_t srow = (uint32_t)(i * MN + acc_row(L, 0, v)) * ldc * 4u;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
+        if constexpr (EDGE)
+          if (acc_col(L, lane, 0) + j * MN >= ncols) continue;
         // the b32 buffer builtins move raw 32-bit patterns: bit-cast, never convert
         float x = acc[i][j][v];
         if constexpr (ACCUM)

@@ -39,7 +39,11 @@ struct Products {
 // Loads one R x BK fp32 operand tile per stage and writes its 16-bit hi (and
 // lo) parts to swizzled LDS tiles.  KC: K contiguous (element (r,k) at
 // base[(r0+r)*ld + k0+k]); otherwise K strided (base[(k0+k)*ld + r0+r]).
-// Each thread moves chunks of 8 values (two 16-byte loads).
+// Each thread moves chunks of 8 values (two 16-byte loads).  EDGE: K positions
+// past k_end, and (K strided) rows past rows_total, are zero; a vector that
+// straddles the edge is read element by element, so no read leaves the
+// operand's storage.  K-contiguous rows past rows_total repeat the last row and
+// are never stored.
 template <int R, int BK, int NT, bool KC, bool EDGE, bool SPLIT, int DT>
 struct SplitLoader {
   static constexpr int CHUNKS = R * BK / 8;
@@ -61,22 +65,24 @@ struct SplitLoader {
         if (!EDGE || kf + 8 <= k_end) {
           reg[i][0] = *reinterpret_cast<const f32x4*>(p);
           reg[i][1] = *reinterpret_cast<const f32x4*>(p + 4);
-        } else {
-          reg[i][0] = kf < k_end ? *reinterpret_cast<const f32x4*>(p) : z;
-          reg[i][1] = kf + 4 < k_end ? *reinterpret_cast<const f32x4*>(p + 4) : z;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (kf + e >= k_end) reg[i][0][e] = 0.f;
-            if (kf + 4 + e >= k_end) reg[i][1][e] = 0.f;
-          }
+        } else {  // K positions past k_end are zero and never read
+          reg[i][0] = gload4_partial(p, k_end - kf);
+          reg[i][1] = gload4_partial(p + 4, k_end - kf - 4);
         }
       } else {
         const int k = idx / (R / 8), rc = idx % (R / 8);
         const int gk = k0 + k, gr = r0 + rc * 8;
         const float* p = base + (int64_t)gk * ld + gr;
-        const bool kin = !EDGE || gk < k_end;
-        reg[i][0] = (kin && (!EDGE || gr < rows_total)) ? *reinterpret_cast<const f32x4*>(p) : z;
-        reg[i][1] = (kin && (!EDGE || gr + 4 < rows_total)) ? *reinterpret_cast<const f32x4*>(p + 4) : z;
+        if (!EDGE || (gk < k_end && gr + 8 <= rows_total)) {
+          reg[i][0] = *reinterpret_cast<const f32x4*>(p);
+          reg[i][1] = *reinterpret_cast<const f32x4*>(p + 4);
+        } else if (gk < k_end) {  // rows past rows_total are zero and never read
+          reg[i][0] = gload4_partial(p, rows_total - gr);
+          reg[i][1] = gload4_partial(p + 4, rows_total - gr - 4);
+        } else {
+          reg[i][0] = z;
+          reg[i][1] = z;
+        }
       }
     }
   }

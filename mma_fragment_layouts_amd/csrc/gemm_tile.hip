@@ -94,21 +94,23 @@ static int launch_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, f
 // feeds the MFMAs.  One barrier per K step both publishes stage kt (every
 // wave's loads for it have landed) and retires stage kt-1, whose buffer the
 // new request reuses.  AKM / BKM: A column-major / B row-major (k-major slabs,
-// fragments read with the transpose read).
-template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT, int STAGES, bool AKM, bool BKM>
+// fragments read with the transpose read).  EDGE: M or N is not a multiple of
+// the tile — the last tile row / column loads zeros (or neighbouring storage)
+// past the edge and stores only the elements inside C.
+template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT, int STAGES, bool AKM, bool BKM, bool EDGE>
 __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t* __restrict__ A,
                                                                    const uint16_t* __restrict__ B,
                                                                    float* __restrict__ C, uint32_t lda, uint32_t ldb,
-                                                                   uint32_t ldc, int K, int tiles_m, int tiles_n,
-                                                                   int accumulate) {
+                                                                   uint32_t ldc, int M, int N, int K, int tiles_m,
+                                                                   int tiles_n, int accumulate) {
   constexpr int BK = 64;
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MN = Shape<SHAPE>::MN;
   constexpr int TM = WM / MN, TN = WN / MN;
   constexpr int STAGE = (BM + BN) * BK;
-  using DA = DmaOperand<SHAPE, BM, NW, AKM>;
-  using DB = DmaOperand<SHAPE, BN, NW, BKM>;
+  using DA = DmaOperand<SHAPE, BM, NW, AKM, EDGE>;
+  using DB = DmaOperand<SHAPE, BN, NW, BKM, EDGE>;
   constexpr int LOADS = DA::INSTR + DB::INSTR;
   static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "vmcnt range");
   using Acc = typename Shape<SHAPE>::Acc;
@@ -124,8 +126,8 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr0 = (wave / WGN) * WM, wc0 = (wave % WGN) * WN;
 
-  const DA da(A, lda, row0, K, wave, lane);
-  const DB db(B, ldb, col0, K, wave, lane);
+  const DA da(A, lda, row0, K, wave, lane, M - row0);
+  const DB db(B, ldb, col0, K, wave, lane, N - col0);
   auto issue = [&](int stage, int k0) {
     da.issue(lds + stage * STAGE, wave, k0);
     db.issue(lds + stage * STAGE + BM * BK, wave, k0);
@@ -152,22 +154,30 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
     const int cur = (kt % STAGES) * STAGE;
     mma_slab<SHAPE, DT, TM, TN, BK>(lds + cur, lds + cur + BM * BK, fa, fb, acc);
   }
-  // The store buffer starts at this wave's tile origin and spans its WM rows.
-  const rsrc_t rc = make_rsrc(C + (int64_t)(row0 + wr0) * ldc + col0 + wc0, (uint32_t)WM * ldc * 4u);
+  // The store buffer starts at this wave's tile origin and spans its WM rows
+  // (EDGE: only the rows inside C).
+  const int wrows = EDGE ? max(0, min(WM, M - (row0 + wr0))) : WM;
+  const rsrc_t rc = make_rsrc(C + (int64_t)(row0 + wr0) * ldc + col0 + wc0, (uint32_t)wrows * ldc * 4u);
+  const int ncols = N - (col0 + wc0);
   if (accumulate)
-    store_acc_rsrc<SHAPE, TM, TN, true>(rc, ldc, lane, acc);
+    store_acc_rsrc<SHAPE, TM, TN, true, EDGE>(rc, ldc, lane, acc, ncols);
   else
-    store_acc_rsrc<SHAPE, TM, TN, false>(rc, ldc, lane, acc);
+    store_acc_rsrc<SHAPE, TM, TN, false, EDGE>(rc, ldc, lane, acc, ncols);
 }
 
 template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT, bool AKM, bool BKM, int STAGES = 2>
 static int launch_fast(const void* a, int64_t lda, const void* b, int64_t ldb, float* c, int64_t ldc, int M, int N,
                        int K, int accumulate, hipStream_t stream) {
-  const int tiles_m = M / BM, tiles_n = N / BN;
-  hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WGM, WGN, SHAPE, DT, STAGES, AKM, BKM>), dim3(tiles_m * tiles_n),
-                     dim3(WGM * WGN * 64), 0,
-                     stream, (const uint16_t*)a, (const uint16_t*)b, c, (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, K,
-                     tiles_m, tiles_n, accumulate);
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const dim3 grid(tiles_m * tiles_n), block(WGM * WGN * 64);
+  const auto A = (const uint16_t*)a;
+  const auto B = (const uint16_t*)b;
+  if (M % BM == 0 && N % BN == 0)
+    hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WGM, WGN, SHAPE, DT, STAGES, AKM, BKM, false>), grid, block, 0, stream,
+                       A, B, c, (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, M, N, K, tiles_m, tiles_n, accumulate);
+  else
+    hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WGM, WGN, SHAPE, DT, STAGES, AKM, BKM, true>), grid, block, 0, stream,
+                       A, B, c, (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, M, N, K, tiles_m, tiles_n, accumulate);
   return launch_status();
 }
 
@@ -194,33 +204,33 @@ static int dispatch_fast(int shape, const void* a, int64_t lda, const void* b, i
   // The largest tile that still gives the chip at least 128 workgroups:
   // 256 x 256 (16 waves of 64 x 64), 128 x 128 (4 waves of 64 x 64), or for
   // small problems with K-contiguous operands 64 x 64 (2 waves of 32 x 64),
-  // where a single big tile would leave all but a few CUs idle.
-  const auto count = [&](int t) { return (int64_t)(M / t) * (N / t); };
+  // where a single big tile would leave all but a few CUs idle.  Sizes that
+  // are not tile multiples run the EDGE variant of the same kernel.
+  const auto count = [&](int t) { return (int64_t)((M + t - 1) / t) * ((N + t - 1) / t); };
   const bool s32 = shape == MFL_MFMA_32X32X16;
-  if (M % 256 == 0 && N % 256 == 0 && count(256) >= 128)
+  if (count(256) >= 128)
     return s32 ? launch_fast<256, 256, 4, 4, 1, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)
                : launch_fast<256, 256, 4, 4, 0, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-  if (M % 128 == 0 && N % 128 == 0 && (count(128) >= 128 || AKM || BKM))
+  if (count(128) >= 128 || AKM || BKM)
     return s32 ? launch_fast<128, 128, 2, 2, 1, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)
                : launch_fast<128, 128, 2, 2, 0, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
   if constexpr (!AKM && !BKM)
-    if (M % 64 == 0 && N % 64 == 0)
-      return s32 ? launch_fast<64, 64, 2, 1, 1, DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)
-                 : launch_fast<64, 64, 2, 1, 0, DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-  return MFL_EUNSUPPORTED;  // not reached: the caller checked the sizes
+    return s32 ? launch_fast<64, 64, 2, 1, 1, DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)
+               : launch_fast<64, 64, 2, 1, 0, DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  return MFL_EUNSUPPORTED;  // not reached: k-major operands always take a 128 or 256 tile
 }
 
-// Whether dispatch_fast has a tile for these sizes.
-static bool fast_tiles(bool any_kmajor, int M, int N) {
-  if (M % 128 == 0 && N % 128 == 0) return true;
-  return !any_kmajor && M % 64 == 0 && N % 64 == 0;
+// Whether dispatch_fast takes these sizes: K a multiple of 64, and an M (N)
+// that a k-major A (B) tile can clamp on a 16-byte chunk boundary.
+static bool fast_sizes(bool akm, bool bkm, int M, int N, int K) {
+  return K % 64 == 0 && K > 0 && (!akm || M % 8 == 0) && (!bkm || N % 8 == 0);
 }
 
 template <int DT>
 static int dispatch(int shape, const void* a, int64_t lda, int oa, const void* b, int64_t ldb, int ob, float* c,
                     int64_t ldc, int M, int N, int K, int accumulate, hipStream_t s) {
   const bool akm = oa == MFL_COL_MAJOR, bkm = ob == MFL_ROW_MAJOR;
-  if (K % 64 == 0 && fast_tiles(akm || bkm, M, N) && fast_fits(akm, lda, K) && fast_fits(bkm, ldb, K) &&
+  if (fast_sizes(akm, bkm, M, N, K) && fast_fits(akm, lda, K) && fast_fits(bkm, ldb, K) &&
       256 * ldc * 4 < ((int64_t)1 << 32)) {
     if (!akm && !bkm) return dispatch_fast<DT, false, false>(shape, a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
     if (!akm) return dispatch_fast<DT, false, true>(shape, a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);

@@ -242,3 +242,43 @@ def test_dense_4096_bf16_other_orders(orders, shape):
     mfl.gemm_tile_mma_shape(shape, mfl.BF16, n, n, n, q16(sa, "bf16"), 4160, oa, q16(sb, "bf16"), 4160, ob, c, n, 0,
                             stream())
     assert torch.equal(c.view(torch.int32), ref.view(torch.int32))
+
+
+# Sizes that are not tile multiples (K a multiple of 64) run the fast kernel's
+# EDGE variant: loads past M / N return zeros (or neighbouring storage) through
+# the buffer extents, and only elements inside C are stored.  C here has
+# ldc = N + 5 with a sentinel in its padding, which must survive; every order
+# must still give the same bits.
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.parametrize("mnk,accumulate", [((200, 136, 128), 0),      # 64 x 64 tiles (K-contiguous), 128 (k-major)
+                                            ((1000, 520, 192), 1),
+                                            ((8, 264, 64), 0),         # fewer rows than one tile
+                                            ((4000, 4000, 256), 0),    # 256 x 256 tiles, ragged last row / column
+                                            ((2056, 1160, 128), 1)])
+def test_fast_path_ragged_all_orders(mnk, accumulate, fmt):
+    m, n, k = mnk
+    rng = np.random.default_rng(m + 7 * n + k)
+    a = rng.uniform(-1, 1, (m, k)).astype(np.float32)
+    b = rng.uniform(-1, 1, (k, n)).astype(np.float32)
+    ldc = n + 5
+    c0 = rng.standard_normal((m, n)).astype(np.float32)
+    ref = R.gemm_ref(a, np.ascontiguousarray(b.T), fmt) + (c0.astype(np.float64) if accumulate else 0.0)
+    first = None
+    for oa, ob in ORDERS:
+        say("gemm fast ragged", m, n, k, fmt, accumulate, oa, ob)
+        sa = storage(a, oa, (k if oa == mfl.ROW_MAJOR else m) + 8)
+        sb = storage(b, ob, (n if ob == mfl.ROW_MAJOR else k) + 8)
+        cs = np.full((m, ldc), 12345.0, np.float32)
+        cs[:, :n] = c0 if accumulate else np.nan
+        c = dev32(cs)
+        mfl.gemm_tile_mma(DT[fmt], m, n, k, q16(sa, fmt), sa.shape[1], oa, q16(sb, fmt), sb.shape[1], ob, c, ldc,
+                          accumulate, stream())
+        ch = host(c)
+        assert np.all(ch[:, n:] == 12345.0), "padding of C was written"
+        out = ch[:, :n]
+        assert not np.isnan(out).any()
+        assert R.rel_error(out, ref) <= TOL
+        if first is None:
+            first = out.copy()
+        else:
+            assert np.array_equal(out.view(np.uint32), first.view(np.uint32)), (oa, ob)
