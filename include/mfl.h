@@ -192,10 +192,11 @@ MFL_API int split_fp32(int dtype, const float *x, void *hi, void *lo, int64_t n,
  * accumulation kept in registers across the whole K loop; each output tile is
  * stored once through the accumulator layout (Warp issue #1965, "Proposed
  * change" and "Design consequences").  Operand orders are free.  The fast path
- * takes K a multiple of 64, M a multiple of 8 when A is column-major and N a
+ * takes K a multiple of 8, M a multiple of 8 when A is column-major and N a
  * multiple of 8 when B is row-major, and buffers within 4 GiB (256 rows of
  * lda / ldb / ldc; K rows of lda for column-major A, of ldb for row-major B);
- * M and N need not be tile multiples (the last tiles are clipped, and nothing
+ * M, N and K need not be tile multiples (the last tiles are clipped, the K
+ * positions of the last slab past k are zeroed in registers, and nothing
  * outside the m x n block of C, padding included, is written).  A
  * column-major A or row-major B is staged K-major in LDS and read with the
  * gfx950 transpose read, with results bit-identical to the K-contiguous

@@ -197,16 +197,29 @@ __device__ __forceinline__ u32x4 frag_read(const uint16_t* s, const KmFrag<SHAPE
 
 // One BK-deep slab of the wave's TM x TN grid of MFMA tiles: for each MFMA K
 // step, read the A and B fragments from LDS and accumulate into registers.
-template <int SHAPE, int DT, int TM, int TN, int BK, class RA, class RB>
+// MASKK: when kvalid < BK only the first kvalid (a multiple of 8) K positions of
+// the slab are real; a lane whose 8 K positions (8*(lane div MN) + i of the K
+// step) lie past them zeroes its A and B fragments, so whatever the LDS holds
+// there never reaches C.
+template <int SHAPE, int DT, int TM, int TN, int BK, bool MASKK = false, class RA, class RB>
 __device__ __forceinline__ void mma_slab(const uint16_t* sA, const uint16_t* sB, const RA& fa, const RB& fb,
-                                         typename Shape<SHAPE>::Acc (&acc)[TM][TN]) {
+                                         typename Shape<SHAPE>::Acc (&acc)[TM][TN], int kvalid = BK) {
+  constexpr int MN = Shape<SHAPE>::MN, KM = Shape<SHAPE>::K;
 #pragma unroll
-  for (int kk = 0; kk < BK / Shape<SHAPE>::K; ++kk) {
+  for (int kk = 0; kk < BK / KM; ++kk) {
     u32x4 a[TM], b[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) a[i] = frag_read(sA, fa, kk, i);
 #pragma unroll
     for (int j = 0; j < TN; ++j) b[j] = frag_read(sB, fb, kk, j);
+    if constexpr (MASKK) {
+      if (kvalid < BK && kk * KM + 8 * ((threadIdx.x & 63) / MN) >= kvalid) {  // kvalid is wave-uniform
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[j] = u32x4{0, 0, 0, 0};
+      }
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -227,12 +240,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 //   k-major (A column-major, B row-major): the kmaj_chunk layout; a load
 //     instruction fills 64 consecutive chunks, 8 K rows x 128 contiguous bytes.
 // Load instruction i of wave w fills bytes (i*NW + w)*1024 .. +1024 of the slab.
-// EDGE: only `valid` (< R) rows / columns of the tile exist.  The buffer extent
-// then ends at the last valid element — K-contiguous: after `valid` rows;
-// k-major: at column `valid` of the last K row — and the loads return zeros
-// from there on (the hardware checks every dword against the extent); columns
-// past `valid` in the earlier K rows of a k-major tile read neighbouring
-// storage.  Either way they only feed outputs that are never stored.
+// EDGE: only `valid` (<= R) rows / columns of the tile exist, and K need not be a
+// multiple of 64.  The buffer extent then ends at the last valid element —
+// K-contiguous: at K in row `valid` - 1; k-major: at column `valid` of the last
+// K row — and the loads return zeros from there on (the hardware checks every
+// dword against the extent).  Other values past the edges come from
+// neighbouring storage: rows / columns past M or N only feed outputs that are
+// never stored, and K positions past K are zeroed in the registers (mma_slab).
 template <int SHAPE, int R, int NW, bool KMAJOR, bool EDGE = false>
 struct DmaOperand {
   static constexpr int INSTR = R / 8 / NW;
@@ -245,7 +259,9 @@ struct DmaOperand {
   uint32_t voff, ld2;
 
   // X: the operand; r0: first M (or N) index of the tile; ld: leading dimension;
-  // valid: M (or N) - r0, used when EDGE.
+  // valid: M (or N) - r0, used when EDGE.  With EDGE a K-contiguous operand's
+  // extent ends at K in its last valid row, so a last slab that reaches past K
+  // reads no element past the operand's storage.
   __device__ __forceinline__ DmaOperand(const uint16_t* X, uint32_t ld, int r0, int K, int wave, int lane,
                                         int valid = R) {
     ld2 = ld * 2u;
@@ -258,7 +274,7 @@ struct DmaOperand {
       kmaj_coords<SHAPE>(wave * 64 + lane, &k, &r);
       voff = (uint32_t)k * ld2 + (uint32_t)r * 2u;
     } else {
-      rs = make_rsrc(X + (int64_t)r0 * ld, v * ld2);
+      rs = make_rsrc(X + (int64_t)r0 * ld, EDGE ? ((v - 1u) * ld + (uint32_t)K) * 2u : v * ld2);
       const int row = wave * 8 + (lane >> 3);
       voff = (uint32_t)row * ld2 + (uint32_t)(((lane & 7) ^ swz<64>(row)) << 4);
     }

@@ -80,7 +80,7 @@ static int launch_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, f
 }
 
 // ---------------------------------------------------------------------------
-// Fast path: M % BM == 0, N % BN == 0, K % 64 == 0, either operand order.
+// Fast path: any operand order; ragged M, N, K through the EDGE variant.
 // Global -> LDS moves use the CDNA4 direct-to-LDS buffer load (DmaOperand: one
 // wave instruction writes 64 x 16 bytes to consecutive LDS addresses, with no
 // staging registers, the layout applied on the source side).  Per-lane state is
@@ -95,8 +95,9 @@ static int launch_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, f
 // wave's loads for it have landed) and retires stage kt-1, whose buffer the
 // new request reuses.  AKM / BKM: A column-major / B row-major (k-major slabs,
 // fragments read with the transpose read).  EDGE: M or N is not a multiple of
-// the tile — the last tile row / column loads zeros (or neighbouring storage)
-// past the edge and stores only the elements inside C.
+// the tile, or K not of 64 — the last tile row / column loads zeros (or
+// neighbouring storage) past the edge and stores only the elements inside C,
+// and the last K slab zeroes the fragments of K positions past K.
 template <int BM, int BN, int WGM, int WGN, int SHAPE, int DT, int STAGES, bool AKM, bool BKM, bool EDGE>
 __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t* __restrict__ A,
                                                                    const uint16_t* __restrict__ B,
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
   Acc acc[TM][TN];
   zero_acc<SHAPE, TM, TN>(acc);
 
-  const int KT = K / BK;
+  const int KT = (K + BK - 1) / BK;  // a multiple of BK unless EDGE
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
     if (st < KT) issue(st, st * BK);
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
     __syncthreads();
     if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
     const int cur = (kt % STAGES) * STAGE;
-    mma_slab<SHAPE, DT, TM, TN, BK>(lds + cur, lds + cur + BM * BK, fa, fb, acc);
+    mma_slab<SHAPE, DT, TM, TN, BK, EDGE>(lds + cur, lds + cur + BM * BK, fa, fb, acc, K - kt * BK);
   }
   // The store buffer starts at this wave's tile origin and spans its WM rows
   // (EDGE: only the rows inside C).
@@ -172,7 +173,7 @@ static int launch_fast(const void* a, int64_t lda, const void* b, int64_t ldb, f
   const dim3 grid(tiles_m * tiles_n), block(WGM * WGN * 64);
   const auto A = (const uint16_t*)a;
   const auto B = (const uint16_t*)b;
-  if (M % BM == 0 && N % BN == 0)
+  if (M % BM == 0 && N % BN == 0 && K % 64 == 0)
     hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WGM, WGN, SHAPE, DT, STAGES, AKM, BKM, false>), grid, block, 0, stream,
                        A, B, c, (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, M, N, K, tiles_m, tiles_n, accumulate);
   else
@@ -220,10 +221,11 @@ static int dispatch_fast(int shape, const void* a, int64_t lda, const void* b, i
   return MFL_EUNSUPPORTED;  // not reached: k-major operands always take a 128 or 256 tile
 }
 
-// Whether dispatch_fast takes these sizes: K a multiple of 64, and an M (N)
-// that a k-major A (B) tile can clamp on a 16-byte chunk boundary.
+// Whether dispatch_fast takes these sizes: K a multiple of 8 (whole 16-byte
+// chunks along K), and an M (N) that a k-major A (B) tile can clamp on a
+// 16-byte chunk boundary.
 static bool fast_sizes(bool akm, bool bkm, int M, int N, int K) {
-  return K % 64 == 0 && K > 0 && (!akm || M % 8 == 0) && (!bkm || N % 8 == 0);
+  return K % 8 == 0 && K > 0 && (!akm || M % 8 == 0) && (!bkm || N % 8 == 0);
 }
 
 template <int DT>

@@ -244,9 +244,10 @@ def test_dense_4096_bf16_other_orders(orders, shape):
     assert torch.equal(c.view(torch.int32), ref.view(torch.int32))
 
 
-# Sizes that are not tile multiples (K a multiple of 64) run the fast kernel's
+# Sizes that are not tile multiples (K a multiple of 8) run the fast kernel's
 # EDGE variant: loads past M / N return zeros (or neighbouring storage) through
-# the buffer extents, and only elements inside C are stored.  C here has
+# the buffer extents, K positions past K are zeroed in the registers, and only
+# elements inside C are stored.  C here has
 # ldc = N + 5 with a sentinel in its padding, which must survive; every order
 # must still give the same bits.
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
@@ -254,7 +255,10 @@ def test_dense_4096_bf16_other_orders(orders, shape):
                                             ((1000, 520, 192), 1),
                                             ((8, 264, 64), 0),         # fewer rows than one tile
                                             ((4000, 4000, 256), 0),    # 256 x 256 tiles, ragged last row / column
-                                            ((2056, 1160, 128), 1)])
+                                            ((2056, 1160, 128), 1),
+                                            ((1000, 520, 200), 0),     # K not a multiple of 64: masked last slab
+                                            ((264, 136, 8), 1),        # a single partial K slab
+                                            ((4000, 4096, 4040), 0)])  # 256 x 256 tiles, every edge ragged
 def test_fast_path_ragged_all_orders(mnk, accumulate, fmt):
     m, n, k = mnk
     rng = np.random.default_rng(m + 7 * n + k)
