@@ -252,10 +252,14 @@ MFL_API int gemm_split_fp32(int piece, int64_t m, int64_t n, int64_t k,
  * (hi and lo of A and of B, each in its operand's storage shape — A: m rows
  * row-major, k rows column-major; B: n rows column-major, k rows row-major —
  * of ld elements, 256-byte aligned) when the planes path applies — both
- * operands MFL_SPLIT, any orders, m % 128 == 0, n % 128 == 0, k % 64 == 0
- * (k > 0), lda % 8 == 0, ldb % 8 == 0, buffers within 4 GiB — and 0 otherwise
- * (then gemm_split_fp32_ws runs the split-on-load kernel, which needs none).  MFL_EINVAL on NULL or unknown
- * orders / modes, MFL_EOVERFLOW if the size does not fit int64. */
+ * operands MFL_SPLIT, any orders, m, n, k > 0, k % 8 == 0, m % 8 == 0 when A
+ * is column-major, n % 8 == 0 when B is row-major, lda % 8 == 0,
+ * ldb % 8 == 0, buffers within 4 GiB (128 rows of lda / ldb; k rows for a
+ * column-major A or row-major B; 64 rows of ldc) — and 0 otherwise (then
+ * gemm_split_fp32_ws runs the split-on-load kernel, which needs none).  m and
+ * n need not be multiples of the 128 x 128 tile, nor k of its 64-deep slab.
+ * MFL_EINVAL on NULL or unknown orders / modes, MFL_EOVERFLOW if the size
+ * does not fit int64. */
 MFL_API int gemm_split_fp32_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t lda, int order_a,
                                             int mode_a, int64_t ldb, int order_b, int mode_b, int64_t ldc,
                                             int64_t *bytes);
@@ -277,7 +281,8 @@ MFL_API int gemm_split_fp32_ws(int piece, int64_t m, int64_t n, int64_t k,
 
 /* gemm_tile_mma with an explicit MFMA instruction for the fast path
  * (MFL_MFMA_16X16X32 or MFL_MFMA_32X32X16); gemm_tile_mma uses 16x16x32.  The
- * generic path (ragged sizes) always uses 16x16x32. */
+ * generic path (k not a multiple of 8, a k-major operand whose m or n is not a
+ * multiple of 8, or buffers past 4 GiB) always uses 16x16x32. */
 MFL_API int gemm_tile_mma_shape(int shape, int dtype, int64_t m, int64_t n, int64_t k,
                                 const void *a, int64_t lda, int order_a,
                                 const void *b, int64_t ldb, int order_b,

@@ -24,13 +24,17 @@ namespace mfl {
 // AKM / BKM: A column-major / B row-major — those planes are staged k-major
 // and read with the transpose read, as in the dense fast path; the MFMAs and
 // their order do not change, so every operand order gives the same bits.
-template <int DT, class P, bool AKM, bool BKM>
+// EDGE: M or N is not a multiple of 128, or K not of 64 — as in the dense fast
+// path, the last tiles load zeros (or neighbouring storage) past the edges, the
+// fragments of K positions past K are zeroed in the last slab, and only the
+// elements inside C are stored.
+template <int DT, class P, bool AKM, bool BKM, bool EDGE>
 __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* __restrict__ Ah,
                                                                 const uint16_t* __restrict__ Al,
                                                                 const uint16_t* __restrict__ Bh,
                                                                 const uint16_t* __restrict__ Bl, float* __restrict__ C,
-                                                                uint32_t lda, uint32_t ldb, uint32_t ldc, int K,
-                                                                int tiles_m, int tiles_n, int accumulate) {
+                                                                uint32_t lda, uint32_t ldb, uint32_t ldc, int M, int N,
+                                                                int K, int tiles_m, int tiles_n, int accumulate) {
   static_assert(P::SA && P::SB, "the planes path splits both operands");
   constexpr int SHAPE = 0, BM = 128, BN = 128, BK = 64, WGM = 2, WGN = 4, NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -39,8 +43,8 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
   constexpr int PLANE = BM * BK;                   // one plane's slab (BM == BN), 16-bit elements
   constexpr int STAGE = 4 * PLANE;                 // A_hi | A_lo | B_hi | B_lo
   static_assert(BM == BN, "planes share one slab size");
-  using DA = DmaOperand<SHAPE, BM, NW, AKM>;
-  using DB = DmaOperand<SHAPE, BN, NW, BKM>;
+  using DA = DmaOperand<SHAPE, BM, NW, AKM, EDGE>;
+  using DB = DmaOperand<SHAPE, BN, NW, BKM, EDGE>;
   static_assert(2 * (DA::INSTR + DB::INSTR) < 64, "vmcnt range");
   using RA = std::conditional_t<AKM, KmFrag<SHAPE, BM, WM, TM>, FragOffsets<SHAPE, BK>>;
   using RB = std::conditional_t<BKM, KmFrag<SHAPE, BN, WN, TN>, FragOffsets<SHAPE, BK>>;
@@ -55,8 +59,8 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr0 = (wave / WGN) * WM, wc0 = (wave % WGN) * WN;
 
-  const DA dah(Ah, lda, row0, K, wave, lane), dal(Al, lda, row0, K, wave, lane);
-  const DB dbh(Bh, ldb, col0, K, wave, lane), dbl(Bl, ldb, col0, K, wave, lane);
+  const DA dah(Ah, lda, row0, K, wave, lane, M - row0), dal(Al, lda, row0, K, wave, lane, M - row0);
+  const DB dbh(Bh, ldb, col0, K, wave, lane, N - col0), dbl(Bl, ldb, col0, K, wave, lane, N - col0);
   auto issue = [&](int stage, int k0) {
     uint16_t* st = lds + stage * STAGE;
     dah.issue(st, wave, k0);
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
 #pragma unroll
   for (int ch = 0; ch < P::CHAINS; ++ch) zero_acc<SHAPE, TM, TN>(acc[ch]);
 
-  const int KT = K / BK;
+  const int KT = (K + BK - 1) / BK;  // a multiple of BK unless EDGE
   if (KT > 0) issue(0, 0);
   for (int kt = 0; kt < KT; ++kt) {
     // this wave's loads of stage kt have landed; after the barrier every
@@ -93,6 +97,17 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
         bh[j] = frag_read(st + 2 * PLANE, fb, kk, j);
         bl[j] = frag_read(st + 3 * PLANE, fb, kk, j);
       }
+      if constexpr (EDGE) {
+        // K positions 8*(lane/16) .. +7 of MFMA step kk (the operand numeral);
+        // the bound is wave-uniform, so only the last slab of a K tail branches
+        const int kvalid = K - kt * BK;
+        if (kvalid < BK && kk * Shape<SHAPE>::K + 8 * (lane / MN) >= kvalid) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) ah[i] = al[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bh[j] = bl[j] = u32x4{0, 0, 0, 0};
+        }
+      }
 #pragma unroll
       for (int p = 0; p < P::NPROD; ++p)
 #pragma unroll
@@ -113,19 +128,27 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
       if constexpr (P::CHAINS == 3) acc[1][i][j] = acc[1][i][j] + acc[2][i][j];
       if constexpr (P::CHAINS >= 2) acc[0][i][j] = acc[0][i][j] + acc[1][i][j];
     }
-  const rsrc_t rc = make_rsrc(C + (int64_t)(row0 + wr0) * ldc + col0 + wc0, (uint32_t)WM * ldc * 4u);
+  // The store buffer spans this wave's rows inside C (EDGE: only those < M).
+  const int wrows = EDGE ? max(0, min(WM, M - (row0 + wr0))) : WM;
+  const rsrc_t rc = make_rsrc(C + (int64_t)(row0 + wr0) * ldc + col0 + wc0, (uint32_t)wrows * ldc * 4u);
+  const int ncols = N - (col0 + wc0);
   if (accumulate)
-    store_acc_rsrc<SHAPE, TM, TN, true>(rc, ldc, lane, acc[0]);
+    store_acc_rsrc<SHAPE, TM, TN, true, EDGE>(rc, ldc, lane, acc[0], ncols);
   else
-    store_acc_rsrc<SHAPE, TM, TN, false>(rc, ldc, lane, acc[0]);
+    store_acc_rsrc<SHAPE, TM, TN, false, EDGE>(rc, ldc, lane, acc[0], ncols);
 }
 
 template <int DT, class P, bool AKM, bool BKM>
 static int launch_planes(const uint16_t* ah, const uint16_t* al, const uint16_t* bh, const uint16_t* bl, float* c,
                          int64_t lda, int64_t ldb, int64_t ldc, int M, int N, int K, int accumulate, hipStream_t s) {
-  const int tiles_m = M / 128, tiles_n = N / 128;
-  hipLaunchKernelGGL((gemm_split_planes_kernel<DT, P, AKM, BKM>), dim3(tiles_m * tiles_n), dim3(512), 0, s, ah, al, bh,
-                     bl, c, (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, K, tiles_m, tiles_n, accumulate);
+  const int tiles_m = (M + 127) / 128, tiles_n = (N + 127) / 128;
+  const dim3 grid(tiles_m * tiles_n), block(512);
+  if (M % 128 == 0 && N % 128 == 0 && K % 64 == 0)
+    hipLaunchKernelGGL((gemm_split_planes_kernel<DT, P, AKM, BKM, false>), grid, block, 0, s, ah, al, bh, bl, c,
+                       (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, M, N, K, tiles_m, tiles_n, accumulate);
+  else
+    hipLaunchKernelGGL((gemm_split_planes_kernel<DT, P, AKM, BKM, true>), grid, block, 0, s, ah, al, bh, bl, c,
+                       (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, M, N, K, tiles_m, tiles_n, accumulate);
   return launch_status();
 }
 
@@ -174,14 +197,17 @@ static int64_t planes_bytes(int64_t m, int64_t n, int64_t k, int64_t lda, int or
   return 2 * align256(rows_a(m, k, order_a) * lda * 2) + 2 * align256(rows_b(n, k, order_b) * ldb * 2);
 }
 
-// The planes path takes both operands split, whole tiles, rows of the planes
-// 16-byte aligned, and 32-bit buffer offsets: a K-contiguous operand's buffer is
-// one 128-row panel, a k-major operand's spans all k rows.
+// The planes path takes both operands split, K a multiple of 8 (whole 16-byte
+// chunks along K), an M (N) that a k-major A (B) tile can clamp on a 16-byte
+// chunk boundary, rows of the planes 16-byte aligned, and 32-bit buffer
+// offsets: a K-contiguous operand's buffer is one 128-row panel, a k-major
+// operand's spans all k rows.  M and N need not be tile multiples.
 static bool planes_apply(int64_t m, int64_t n, int64_t k, int64_t lda, int order_a, int mode_a, int64_t ldb,
                          int order_b, int mode_b, int64_t ldc) {
   const int64_t lim = (int64_t)1 << 32;
   if (mode_a != MFL_SPLIT || mode_b != MFL_SPLIT) return false;
-  if (m % 128 != 0 || n % 128 != 0 || k % 64 != 0 || k <= 0 || lda % 8 != 0 || ldb % 8 != 0) return false;
+  if (m <= 0 || n <= 0 || k <= 0 || k % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0) return false;
+  if ((order_a == MFL_COL_MAJOR && m % 8 != 0) || (order_b == MFL_ROW_MAJOR && n % 8 != 0)) return false;
   const int64_t pa = order_a == MFL_ROW_MAJOR ? 128 : k, pb = order_b == MFL_COL_MAJOR ? 128 : k;
   return pa * lda * 2 < lim && pb * ldb * 2 < lim && 64 * ldc * 4 < lim;
 }

@@ -325,10 +325,16 @@ def test_split_planes_workspace_size(lib):
         2 * al(640 * 520 * 2) + 2 * al(640 * 392 * 2)
     assert lib.gemm_split_fp32_workspace_bytes(512, 384, 640, 648, R_, S_, 392, R_, S_, 384) == \
         2 * al(512 * 648 * 2) + 2 * al(640 * 392 * 2)
+    # ragged M, N and K (a multiple of 8) take the planes path as well
+    assert lib.gemm_split_fp32_workspace_bytes(500, 390, 600, 648, R_, S_, 664, C_, S_, 392) == \
+        2 * al(500 * 648 * 2) + 2 * al(390 * 664 * 2)
+    assert lib.gemm_split_fp32_workspace_bytes(504, 392, 600, 512, C_, S_, 400, R_, S_, 392) == \
+        2 * al(600 * 512 * 2) + 2 * al(600 * 400 * 2)
     # not applicable: no workspace (the split-on-load kernel runs)
     for args in [(512, 384, 640, 648, R_, Rd, 664, C_, S_, 384),   # A rounded
-                 (500, 384, 640, 648, R_, S_, 664, C_, S_, 384),   # M % 128
-                 (512, 384, 600, 648, R_, S_, 664, C_, S_, 384),   # K % 64
+                 (512, 384, 602, 648, R_, S_, 664, C_, S_, 384),   # K % 8
+                 (500, 384, 640, 504, C_, S_, 664, C_, S_, 384),   # column-major A, M % 8
+                 (512, 390, 640, 648, R_, S_, 392, R_, S_, 392),   # row-major B, N % 8
                  (512, 384, 640, 644, R_, S_, 664, C_, S_, 384)]:  # lda % 8
         assert lib.gemm_split_fp32_workspace_bytes(*args) == 0
     with pytest.raises(lib.MflError):

@@ -123,28 +123,35 @@ def test_split_full_size_sampled():
 
 # ---- planes path (gemm_split_fp32_ws): operands split once into hi / lo planes
 
-def run_both(a, bt, chains, lolo, piece, accumulate=0, seed=0, oa=mfl.ROW_MAJOR, ob=mfl.COL_MAJOR):
+SENTINEL = 12345.0
+
+
+def run_both(a, bt, chains, lolo, piece, accumulate=0, seed=0, oa=mfl.ROW_MAJOR, ob=mfl.COL_MAJOR, ldc=None):
     """The same product through gemm_split_fp32 (split on load) and
     gemm_split_fp32_ws (planes), A (M x K) and B (K x N, given as bt = B^T)
     stored in orders oa / ob; leading dimensions padded with NaN and different
-    for A and B; C preset to random values when accumulating."""
+    for A and B; C preset to random values when accumulating.  With ldc > N
+    the padding columns of C hold a sentinel that neither call may touch."""
     m, k = a.shape
     n = bt.shape[0]
+    ldc = n if ldc is None else ldc
     sa = a if oa == mfl.ROW_MAJOR else np.ascontiguousarray(a.T)     # storage rows x inner
     sb = bt if ob == mfl.COL_MAJOR else np.ascontiguousarray(bt.T)
     lda = sa.shape[1] + (-sa.shape[1]) % 8 + 8
     ldb = sb.shape[1] + (-sb.shape[1]) % 8 + 24
     da, db = dev32(padded(sa, lda)), dev32(padded(sb, ldb))
-    wsb = mfl.gemm_split_fp32_workspace_bytes(m, n, k, lda, oa, mfl.SPLIT, ldb, ob, mfl.SPLIT, n)
+    wsb = mfl.gemm_split_fp32_workspace_bytes(m, n, k, lda, oa, mfl.SPLIT, ldb, ob, mfl.SPLIT, ldc)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=device())
-    c0 = np.random.default_rng(seed).standard_normal((m, n)).astype(np.float32) if accumulate else \
-        np.full((m, n), np.nan, np.float32)
+    c0 = np.full((m, ldc), SENTINEL, np.float32)
+    c0[:, :n] = np.random.default_rng(seed).standard_normal((m, n)).astype(np.float32) if accumulate else np.nan
     c_load, c_planes = dev32(c0), dev32(c0)
-    mfl.gemm_split_fp32(DT[piece], m, n, k, da, lda, oa, mfl.SPLIT, db, ldb, ob, mfl.SPLIT, chains, lolo, c_load, n,
+    mfl.gemm_split_fp32(DT[piece], m, n, k, da, lda, oa, mfl.SPLIT, db, ldb, ob, mfl.SPLIT, chains, lolo, c_load, ldc,
                         accumulate, stream())
     mfl.gemm_split_fp32_ws(DT[piece], m, n, k, da, lda, oa, mfl.SPLIT, db, ldb, ob, mfl.SPLIT, chains, lolo, c_planes,
-                           n, accumulate, ws, wsb, stream())
-    return host(c_load), host(c_planes), wsb
+                           ldc, accumulate, ws, wsb, stream())
+    hl, hp = host(c_load), host(c_planes)
+    assert (hl[:, n:] == SENTINEL).all() and (hp[:, n:] == SENTINEL).all(), "C padding written"
+    return hl[:, :n], hp[:, :n], wsb
 
 
 @pytest.mark.parametrize("accumulate", [0, 1])
@@ -171,9 +178,9 @@ def test_split_planes_against_oracle(medium, chains):
 
 
 def test_split_planes_not_applicable_falls_back():
-    """M not a multiple of 128: no workspace is needed and the call is the
+    """K not a multiple of 8: no workspace is needed and the call is the
     split-on-load kernel (identical result)."""
-    a, bt = inputs.gemm_split(200, 384, 640)
+    a, bt = inputs.gemm_split(200, 384, 602)
     say("split planes fallback")
     c_load, c_ws, wsb = run_both(a, bt, 3, 0, "bf16")
     assert wsb == 0
@@ -213,6 +220,38 @@ def test_split_planes_k_strided_against_oracle(medium):
     a, bt, ref, exp3, _ = medium
     say("split planes strided oracle")
     _, c, wsb = run_both(a, bt, 3, 0, "bf16", oa=mfl.COL_MAJOR, ob=mfl.ROW_MAJOR)
+    assert wsb > 0
+    assert R.rel_error(c, ref) <= 5e-6
+    assert R.rel_error(c, exp3) <= 2e-6
+
+
+# Sizes that are not tile multiples take the planes path through its EDGE
+# variant (clipped loads, the last K slab masked in registers, stores only
+# inside C); the MFMAs per accumulator are still those of split on load.
+ORDERS4 = [(mfl.ROW_MAJOR, mfl.COL_MAJOR)] + STRIDED
+RAGGED = [((200, 136, 128), "bf16", 3, 0, 0), ((136, 264, 72), "f16", 2, 0, 1), ((1000, 520, 200), "bf16", 1, 1, 0),
+          ((8, 264, 64), "bf16", 2, 1, 1), ((264, 8, 8), "f16", 3, 0, 0), ((392, 256, 648), "bf16", 3, 1, 1)]
+
+
+@pytest.mark.parametrize("orders", ORDERS4)
+@pytest.mark.parametrize("mnk,piece,chains,lolo,accumulate", RAGGED)
+def test_split_planes_ragged_bit_identical(orders, mnk, piece, chains, lolo, accumulate):
+    m, n, k = mnk
+    a, bt = inputs.gemm_split(m, n, k)
+    say("split planes ragged", orders, mnk, piece, chains, lolo, accumulate)
+    c_load, c_planes, wsb = run_both(a, bt, chains, lolo, piece, accumulate, seed=m + n, oa=orders[0], ob=orders[1],
+                                     ldc=n + 5)
+    assert wsb > 0
+    assert not np.isnan(c_planes).any()
+    assert np.array_equal(c_load.view(np.uint32), c_planes.view(np.uint32))
+
+
+def test_split_planes_ragged_against_oracle():
+    """1000 x 520 x 200 through the planes path: within the oracle bounds."""
+    a, bt = inputs.gemm_split(1000, 520, 200)
+    say("split planes ragged oracle")
+    ref, exp3 = R.split_ref(a, bt), R.split_expansion(a, bt, "bf16")
+    _, c, wsb = run_both(a, bt, 3, 0, "bf16", ldc=523)
     assert wsb > 0
     assert R.rel_error(c, ref) <= 5e-6
     assert R.rel_error(c, exp3) <= 2e-6
