@@ -13,7 +13,11 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Device calls only enqueue work and return; results are ready when the
  *    stream is synchronised.  Calls on one stream are ordered; calls on
- *    different streams that write the same memory race.
+ *    different streams that write the same memory race.  A device call
+ *    launches kernels and nothing else (no allocation, copy, fill or
+ *    synchronisation), so it may be captured in a HIP graph and replayed;
+ *    a replay recomputes everything from the operands, the workspace
+ *    included.
  *  - Matrices: A is M x K, B is K x N, C is M x N.  A row-major A stores
  *    A[m][k] at a[m*lda + k]; a column-major A stores it at a[k*lda + m].  A
  *    row-major B stores B[k][n] at b[k*ldb + n]; a column-major B at
