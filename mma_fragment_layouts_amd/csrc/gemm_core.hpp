@@ -213,7 +213,7 @@ __device__ __forceinline__ void mma_slab(const uint16_t* sA, const uint16_t* sB,
 #pragma unroll
     for (int j = 0; j < TN; ++j) b[j] = frag_read(sB, fb, kk, j);
     if constexpr (MASKK) {
-      if (kvalid < BK && kk * KM + 8 * ((threadIdx.x & 63) / MN) >= kvalid) {  // kvalid is wave-uniform
+      if (kvalid < BK && kk * KM + 8 * ((int)(threadIdx.x & 63) / MN) >= kvalid) {  // kvalid is wave-uniform
 #pragma unroll
         for (int i = 0; i < TM; ++i) a[i] = u32x4{0, 0, 0, 0};
 #pragma unroll
