@@ -12,6 +12,9 @@
 // runs the block MMA and writes C back, with a workgroup barrier between calls.
 // It exists to measure the two costs the issue names — bank conflicts of
 // fragment reads from plain layouts, and the C round trip — on this hardware.
+// In the register arm a repeat of one MFMA K step (TK = 32) reads the next
+// repeat's fragments while its MFMAs issue; deeper repeats overlap inside the
+// repeat instead.
 #include "gemm_core.hpp"
 
 namespace mfl {
@@ -51,10 +54,42 @@ __global__ __launch_bounds__(WGM* WGN * 64) void block_repeat_kernel(const uint1
     }
     __syncthreads();
     const FragOffsets<SHAPE, TK> fa(wr0, lane), fb(wc0, lane);
-    for (int r = 0; r < repeats; ++r) {
-      // Each repeat is a separate block GEMM: its fragments come from LDS again.
-      asm volatile("" ::: "memory");
-      mma_slab<SHAPE, DT, FM, FN, TK>(lds, lds + TM_ * TK, fa, fb, acc);
+    constexpr int KS = TK / Shape<SHAPE>::K;  // MFMA K steps per repeat
+    if constexpr (KS > 1) {
+      for (int r = 0; r < repeats; ++r) {
+        // Each repeat is a separate block GEMM: its fragments come from LDS
+        // again (the memory clobber keeps the compiler from reusing registers).
+        // Within a repeat the reads of K step kk+1 overlap the MFMAs of kk.
+        asm volatile("" ::: "memory");
+        mma_slab<SHAPE, DT, FM, FN, TK>(lds, lds + TM_ * TK, fa, fb, acc);
+      }
+    } else {
+      // One MFMA K step per repeat: the next repeat's fragments are read from
+      // LDS (after the clobber, so they are read again) into the other of two
+      // register sets while this repeat's MFMAs issue.  Same MFMAs, same order.
+      u32x4 xa[2][FM], xb[2][FN];
+      auto rd = [&](int f) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < FM; ++i) xa[f][i] = frag_read(lds, fa, 0, i);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) xb[f][j] = frag_read(lds + TM_ * TK, fb, 0, j);
+      };
+      auto mm = [&](int f) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma<SHAPE, DT>(xa[f][i], xb[f][j], acc[i][j]);
+      };
+      if (repeats > 0) rd(0);
+      int r = 0;
+      for (; r + 1 < repeats; r += 2) {
+        rd(1);
+        mm(0);
+        if (r + 2 < repeats) rd(0);
+        mm(1);
+      }
+      if (r < repeats) mm(0);
     }
   } else {
     // Plain tiles: A rows (row-major, K contiguous), B columns (K contiguous),
