@@ -25,8 +25,10 @@ int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, co
 
 namespace {
 
-constexpr int kSoftmaxThreads = 256;
-constexpr int kSoftmaxVec = 32;  // f32x4 per thread: rows up to 32768 stay in registers
+constexpr int kSoftmaxThreads = 512;
+constexpr int kSoftmaxVec = 16;  // f32x4 per thread: rows up to 32768 stay in registers
+// P~ = exp(s - m) is taken as 2^((s - m) log2 e) with the hardware exp2.
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -39,7 +41,7 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Block-wide reduction of one value per thread (256 threads, 4 waves).
+// Block-wide reduction of one value per thread (kSoftmaxThreads threads).
 template <bool MAX>
 __device__ __forceinline__ float block_reduce(float x, float* red) {
   x = MAX ? wave_max(x) : wave_sum(x);
@@ -54,8 +56,9 @@ __device__ __forceinline__ float block_reduce(float x, float* red) {
 }
 
 // One workgroup per row; the row (n <= 32768, n % 4 == 0) is read once into
-// registers, P~ written back in place, m and l written per row.  The row sum
-// adds each thread's values in order, then the threads' partial sums.
+// registers (non-temporal loads: S is not read again), P~ written back in
+// place, m and l written per row.  The row sum adds each thread's values in
+// order, then the threads' partial sums.
 __global__ __launch_bounds__(kSoftmaxThreads) void softmax_rows_regs(float* __restrict__ S, int64_t lds_, int n,
                                                                    float* __restrict__ m_out,
                                                                    float* __restrict__ l_out) {
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(kSoftmaxThreads) void softmax_rows_regs(float* __re
   for (int i = 0; i < kSoftmaxVec; ++i) {
     const int c = (i * kSoftmaxThreads + threadIdx.x) * 4;
     if (c < n) {
-      v[i] = *reinterpret_cast<const f32x4*>(row + c);
+      v[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + c));
       mx = fmaxf(mx, fmaxf(fmaxf(v[i][0], v[i][1]), fmaxf(v[i][2], v[i][3])));
     }
   }
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(kSoftmaxThreads) void softmax_rows_regs(float* __re
       f32x4 p;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        p[e] = expf(v[i][e] - mx);
+        p[e] = __builtin_amdgcn_exp2f((v[i][e] - mx) * kLog2e);
         sum += p[e];
       }
       *reinterpret_cast<f32x4*>(row + c) = p;
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(kSoftmaxThreads) void softmax_rows_2pass(float* __r
     f32x4 p = *reinterpret_cast<const f32x4*>(row + c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      p[e] = expf(p[e] - mx);
+      p[e] = __builtin_amdgcn_exp2f((p[e] - mx) * kLog2e);
       sum += p[e];
     }
     *reinterpret_cast<f32x4*>(row + c) = p;
