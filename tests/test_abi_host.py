@@ -391,3 +391,26 @@ def test_plain_c_program_uses_the_header_and_library(tmp_path):
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, run.stderr
     assert "ok" in run.stdout
+
+
+def device_program_command(cc, out):
+    """Compile line of tests/c/abi_device_gemm.c: plain C99 against mfl.h and
+    the HIP runtime's C API, linked with libmfl.so and libamdhip64."""
+    from mma_fragment_layouts_amd import _binding
+    libdir = os.path.dirname(_binding.LIB_PATH)
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return [cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+            "-I", os.path.join(rocm, "include"), os.path.join(ROOT, "tests", "c", "abi_device_gemm.c"), "-L", libdir,
+            "-lmfl", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm", f"-Wl,-rpath,{libdir}",
+            f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", str(out)]
+
+
+def test_plain_c_device_program_builds(tmp_path):
+    """The device-side C example (run by the GPU tests) compiles warning-free."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("no C compiler or HIP headers on this host")
+    r = subprocess.run(device_program_command(cc, tmp_path / "abi_device_gemm"), capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
