@@ -227,7 +227,8 @@ def gemm_256(torch, mfl, inputs, stream, dev, q16, out):
 def gemm_orders(torch, mfl, inputs, stream, dev, q16, out):
     """The 4096^3 bf16 GEMM in each operand order (ld 4160, NaN padding).  A
     column-major or B row-major operand is staged as k-major LDS slabs and read
-    with the transpose read."""
+    with the transpose read.  Also the K-contiguous order with fp16 operands and
+    with the 32x32x16 instruction."""
     a, bt = inputs.gemm_dense()
     n = 4096
 
@@ -251,6 +252,16 @@ def gemm_orders(torch, mfl, inputs, stream, dev, q16, out):
                                                  "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
             del da, db
     out["gemm_4096_bf16_orders"] = res
+    # The K-contiguous order with fp16 operands, and with the 32x32x16 instruction.
+    var = {}
+    for label, dt, shape in (("f16_16x16x32", mfl.F16, 0), ("bf16_32x32x16", mfl.BF16, 1)):
+        da, db = q16(a, dt), q16(bt, dt)
+        ms = best_of(lambda: mfl.gemm_tile_mma_shape(shape, dt, n, n, n, da, 4160, mfl.ROW_MAJOR, db, 4160,
+                                                     mfl.COL_MAJOR, c, n, 0, stream), stream)
+        tf = 2 * n ** 3 / ms / 1e9
+        var[label] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del da, db
+    out["gemm_4096_variants"] = var
 
 
 def block_repeat(torch, mfl, inputs, stream, dev, q16, out):
