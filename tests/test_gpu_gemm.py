@@ -137,25 +137,26 @@ def test_fast_path_padded_nan(shape):
     assert R.rel_error(ch, R.gemm_ref(a[:, :1024], bt[:, :1024], "bf16")) <= TOL
 
 
-@pytest.mark.parametrize("shape", [0, 1])
-def test_dense_4096_bf16_sampled(shape):
-    """The 4096^3 bf16 GEMM exactly as the benchmark launches it (A row-major,
-    B column-major, ld 4160 with NaN padding, C fp32 ldc 4096): no NaN anywhere,
-    48 full rows within 1e-5 normwise, and 4096 sampled entries elementwise."""
+@pytest.mark.parametrize("shape,fmt", [(0, "bf16"), (1, "bf16"), (0, "f16"), (1, "f16")])
+def test_dense_4096_bf16_sampled(shape, fmt):
+    """The 4096^3 GEMM exactly as the benchmark launches it (A row-major, B
+    column-major, ld 4160 with NaN padding, C fp32 ldc 4096), in bf16 and, as
+    the benchmark's variant leg runs it, fp16: no NaN anywhere, 48 full rows
+    within 1e-5 normwise, and 4096 sampled entries elementwise."""
     a, bt = inputs.gemm_dense()
-    say("dense 4096^3", shape)
+    say("dense 4096^3", shape, fmt)
     c = torch.full((4096, 4096), np.nan, device=device())
-    mfl.gemm_tile_mma_shape(shape, mfl.BF16, 4096, 4096, 4096, q16(a, "bf16"), 4160, mfl.ROW_MAJOR,
-                            q16(bt, "bf16"), 4160, mfl.COL_MAJOR, c, 4096, 0, stream())
+    mfl.gemm_tile_mma_shape(shape, DT[fmt], 4096, 4096, 4096, q16(a, fmt), 4160, mfl.ROW_MAJOR,
+                            q16(bt, fmt), 4160, mfl.COL_MAJOR, c, 4096, 0, stream())
     ch = host(c)
     assert not np.isnan(ch).any()
     rng = np.random.default_rng(11)
     rows = rng.choice(4096, 48, replace=False)
-    ref_rows = R.gemm_ref(a[rows, :4096], bt[:, :4096], "bf16")
+    ref_rows = R.gemm_ref(a[rows, :4096], bt[:, :4096], fmt)
     assert R.rel_error(ch[rows], ref_rows) <= TOL
     r = rng.integers(0, 4096, 4096)
     cc = rng.integers(0, 4096, 4096)
-    ref = R.gemm_ref_entries(a[:, :4096], bt[:, :4096], "bf16", r, cc)
+    ref = R.gemm_ref_entries(a[:, :4096], bt[:, :4096], fmt, r, cc)
     # elementwise: fp32 accumulation of 4096 products, bound ~ K * u32 * sum|a||b|
     scale = np.abs(ref).max()
     assert np.max(np.abs(ch[r, cc] - ref)) <= 4096 * 2.0 ** -24 * 64 * max(scale, 1.0)
