@@ -95,6 +95,9 @@ def _ptr(x) -> Optional[int]:
     if isinstance(x, int):
         return x
     if hasattr(x, "data_ptr"):
+        # a host tensor's address handed to a kernel would fault the GPU
+        if getattr(x, "is_cuda", True) is False:
+            raise TypeError("expected a device tensor, got one in host memory")
         return x.data_ptr()
     raise TypeError(f"expected a device pointer (int or tensor), got {type(x)}")
 

@@ -414,3 +414,15 @@ def test_plain_c_device_program_builds(tmp_path):
         pytest.skip("no C compiler or HIP headers on this host")
     r = subprocess.run(device_program_command(cc, tmp_path / "abi_device_gemm"), capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_host_tensors_are_refused_before_the_library_is_called(lib):
+    """A host (CPU) tensor's address must never reach a kernel: the binding
+    raises before calling into the library."""
+    import torch
+    a = torch.zeros((64, 64), dtype=torch.int16)
+    c = torch.zeros((64, 64), dtype=torch.float32)
+    with pytest.raises(TypeError, match="host memory"):
+        lib.gemm_tile_mma(lib.BF16, 64, 64, 64, a, 64, lib.ROW_MAJOR, a, 64, lib.COL_MAJOR, c, 64, 0, None)
+    with pytest.raises(TypeError, match="host memory"):
+        lib.quantize_fp32(lib.BF16, c, a, 64, None)
