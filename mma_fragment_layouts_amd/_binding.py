@@ -4,7 +4,9 @@ Every function here has the name of the C entry point it calls (include/mfl.h)
 and does nothing but convert arguments (device pointers from ints or from
 objects with ``data_ptr()``, streams from ints or from objects with
 ``cuda_stream``), call the library and turn a non-zero status into
-``MflError``.  All computation happens in the library's HIP kernels; if the
+``MflError``.  Tensor arguments are also checked, before the call, to be in
+device memory and to hold the region the call touches (the C ABI sees plain
+pointers and cannot).  All computation happens in the library's HIP kernels; if the
 library is missing, the first call raises.
 """
 from __future__ import annotations
@@ -100,6 +102,34 @@ def _ptr(x) -> Optional[int]:
             raise TypeError("expected a device tensor, got one in host memory")
         return x.data_ptr()
     raise TypeError(f"expected a device pointer (int or tensor), got {type(x)}")
+
+
+def _room(x) -> Optional[int]:
+    """Bytes addressable from a tensor's data pointer (to the end of its
+    storage), or None when x is a plain integer pointer."""
+    if not hasattr(x, "untyped_storage"):
+        return None
+    return x.untyped_storage().nbytes() - x.storage_offset() * x.element_size()
+
+
+def _extent(outer: int, inner: int, ld: int, elem: int) -> int:
+    """Bytes spanned by `outer` rows of `ld` elements whose last row holds
+    `inner` elements (an operand's minimum storage)."""
+    return 0 if outer <= 0 or inner <= 0 else ((outer - 1) * ld + inner) * elem
+
+
+def _op(rows: int, cols: int, ld: int, order: int, elem: int) -> int:
+    """Minimum storage of a rows x cols matrix stored in `order`."""
+    return _extent(rows, cols, ld, elem) if order == ROW_MAJOR else _extent(cols, rows, ld, elem)
+
+
+def _need(fn: str, **bufs) -> None:
+    """Raise before the call if a tensor argument is smaller than the region the
+    call will touch: a kernel would otherwise read or write past it."""
+    for name, (x, nbytes) in bufs.items():
+        room = _room(x)
+        if room is not None and nbytes > room:
+            raise ValueError(f"{fn}: `{name}` needs {nbytes} bytes from its data pointer; the tensor holds {room}")
 
 
 def _stream(s) -> Optional[int]:
@@ -214,36 +244,47 @@ def mfma_probe(shape, dtype, a_frag, b_frag, c_in, acc, stream=None) -> None:
 
 
 def quantize_fp32(dtype, x, out, n, stream=None) -> None:
+    _need("quantize_fp32", x=(x, max(n, 0) * 4), out=(out, max(n, 0) * 2))
     _check(load().quantize_fp32(dtype, _ptr(x), _ptr(out), n, _stream(stream)), "quantize_fp32")
 
 
 def split_fp32(dtype, x, hi, lo, n, stream=None) -> None:
+    _need("split_fp32", x=(x, max(n, 0) * 4), hi=(hi, max(n, 0) * 2), lo=(lo, max(n, 0) * 2))
     _check(load().split_fp32(dtype, _ptr(x), _ptr(hi), _ptr(lo), n, _stream(stream)), "split_fp32")
 
 
 def gemm_tile_mma(dtype, m, n, k, a, lda, order_a, b, ldb, order_b, c, ldc, accumulate=0, stream=None) -> None:
+    _need("gemm_tile_mma", a=(a, _op(m, k, lda, order_a, 2)), b=(b, _op(k, n, ldb, order_b, 2)),
+          c=(c, _extent(m, n, ldc, 4)))
     _check(load().gemm_tile_mma(dtype, m, n, k, _ptr(a), lda, order_a, _ptr(b), ldb, order_b, _ptr(c), ldc,
                                 accumulate, _stream(stream)), "gemm_tile_mma")
 
 
 def gemm_tile_mma_shape(shape, dtype, m, n, k, a, lda, order_a, b, ldb, order_b, c, ldc, accumulate=0,
                         stream=None) -> None:
+    _need("gemm_tile_mma_shape", a=(a, _op(m, k, lda, order_a, 2)), b=(b, _op(k, n, ldb, order_b, 2)),
+          c=(c, _extent(m, n, ldc, 4)))
     _check(load().gemm_tile_mma_shape(shape, dtype, m, n, k, _ptr(a), lda, order_a, _ptr(b), ldb, order_b, _ptr(c),
                                       ldc, accumulate, _stream(stream)), "gemm_tile_mma_shape")
 
 
 def gemm_block_repeat(dtype, tm, tn, tk, threads, repeats, m, n, a, b, c, stream=None) -> None:
+    _need("gemm_block_repeat", a=(a, _extent(m, tk, tk, 2)), b=(b, _extent(n, tk, tk, 2)), c=(c, _extent(m, n, n, 4)))
     _check(load().gemm_block_repeat(dtype, tm, tn, tk, threads, repeats, m, n, _ptr(a), _ptr(b), _ptr(c),
                                     _stream(stream)), "gemm_block_repeat")
 
 
 def gemm_block_repeat_lds_api(dtype, tm, tn, tk, threads, repeats, m, n, a, b, c, stream=None) -> None:
+    _need("gemm_block_repeat_lds_api", a=(a, _extent(m, tk, tk, 2)), b=(b, _extent(n, tk, tk, 2)),
+          c=(c, _extent(m, n, n, 4)))
     _check(load().gemm_block_repeat_lds_api(dtype, tm, tn, tk, threads, repeats, m, n, _ptr(a), _ptr(b), _ptr(c),
                                             _stream(stream)), "gemm_block_repeat_lds_api")
 
 
 def gemm_split_fp32(piece, m, n, k, a, lda, order_a, mode_a, b, ldb, order_b, mode_b, chains, lolo, c, ldc,
                     accumulate=0, stream=None) -> None:
+    _need("gemm_split_fp32", a=(a, _op(m, k, lda, order_a, 4)), b=(b, _op(k, n, ldb, order_b, 4)),
+          c=(c, _extent(m, n, ldc, 4)))
     _check(load().gemm_split_fp32(piece, m, n, k, _ptr(a), lda, order_a, mode_a, _ptr(b), ldb, order_b, mode_b,
                                   chains, lolo, _ptr(c), ldc, accumulate, _stream(stream)), "gemm_split_fp32")
 
@@ -257,6 +298,8 @@ def gemm_split_fp32_workspace_bytes(m, n, k, lda, order_a, mode_a, ldb, order_b,
 
 def gemm_split_fp32_ws(piece, m, n, k, a, lda, order_a, mode_a, b, ldb, order_b, mode_b, chains, lolo, c, ldc,
                        accumulate, workspace, workspace_bytes, stream=None) -> None:
+    _need("gemm_split_fp32_ws", a=(a, _op(m, k, lda, order_a, 4)), b=(b, _op(k, n, ldb, order_b, 4)),
+          c=(c, _extent(m, n, ldc, 4)), workspace=(workspace, max(workspace_bytes, 0)))
     _check(load().gemm_split_fp32_ws(piece, m, n, k, _ptr(a), lda, order_a, mode_a, _ptr(b), ldb, order_b, mode_b,
                                      chains, lolo, _ptr(c), ldc, accumulate, _ptr(workspace), workspace_bytes,
                                      _stream(stream)), "gemm_split_fp32_ws")
@@ -269,5 +312,7 @@ def attention_workspace_bytes(nq, nk, d, algo=1) -> int:
 
 
 def attention_split_fp32(nq, nk, d, q, k, v, chains, algo, o, workspace, workspace_bytes, stream=None) -> None:
+    _need("attention_split_fp32", q=(q, _extent(nq, d, d, 4)), k=(k, _extent(nk, d, d, 4)),
+          v=(v, _extent(nk, d, d, 4)), o=(o, _extent(nq, d, d, 4)), workspace=(workspace, max(workspace_bytes, 0)))
     _check(load().attention_split_fp32(nq, nk, d, _ptr(q), _ptr(k), _ptr(v), chains, algo, _ptr(o),
                                        _ptr(workspace), workspace_bytes, _stream(stream)), "attention_split_fp32")

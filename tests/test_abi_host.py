@@ -426,3 +426,65 @@ def test_host_tensors_are_refused_before_the_library_is_called(lib):
         lib.gemm_tile_mma(lib.BF16, 64, 64, 64, a, 64, lib.ROW_MAJOR, a, 64, lib.COL_MAJOR, c, 64, 0, None)
     with pytest.raises(TypeError, match="host memory"):
         lib.quantize_fp32(lib.BF16, c, a, 64, None)
+
+
+class _DeviceTensorStandIn:
+    """Looks like a device tensor to the binding (is_cuda, storage size) but has
+    no memory behind it; only used where the binding must refuse the call."""
+    is_cuda = True
+
+    def __init__(self, nbytes, elem=2, offset=0):
+        self._nbytes, self._elem, self._offset = nbytes, elem, offset
+
+    def untyped_storage(self):
+        outer = self
+
+        class _S:
+            def nbytes(self):
+                return outer._nbytes
+        return _S()
+
+    def storage_offset(self):
+        return self._offset
+
+    def element_size(self):
+        return self._elem
+
+    def data_ptr(self):
+        raise AssertionError("the binding must refuse before taking the pointer")
+
+
+def test_undersized_tensors_are_refused_before_the_library_is_called(lib):
+    T = _DeviceTensorStandIn
+    m = n = k = 256
+    ok16, ok32 = T(m * k * 2), T(m * n * 4, elem=4)
+    # C one element short (ldc 256: 256 * 256 fp32 needed)
+    with pytest.raises(ValueError, match="`c`"):
+        lib.gemm_tile_mma(lib.BF16, m, n, k, ok16, k, lib.ROW_MAJOR, ok16, k, lib.COL_MAJOR,
+                          T(m * n * 4 - 4, elem=4), n, 0, None)
+    # A stored with a padded leading dimension needs (m - 1) * lda + k elements
+    with pytest.raises(ValueError, match="`a`"):
+        lib.gemm_tile_mma(lib.BF16, m, n, k, T(m * k * 2), k + 64, lib.ROW_MAJOR, ok16, k, lib.COL_MAJOR, ok32, n, 0,
+                          None)
+    # a view that starts inside its storage has less room
+    with pytest.raises(ValueError, match="`b`"):
+        lib.gemm_tile_mma(lib.BF16, m, n, k, ok16, k, lib.ROW_MAJOR, T(m * k * 2, offset=8), k, lib.COL_MAJOR, ok32,
+                          n, 0, None)
+    with pytest.raises(ValueError, match="`out`"):
+        lib.quantize_fp32(lib.BF16, T(1024 * 4, elem=4), T(1023 * 2), 1024, None)
+    with pytest.raises(ValueError, match="`workspace`"):
+        lib.gemm_split_fp32_ws(lib.BF16, m, n, k, T(m * k * 4, elem=4), k, lib.ROW_MAJOR, lib.SPLIT,
+                               T(n * k * 4, elem=4), k, lib.COL_MAJOR, lib.SPLIT, 2, 0, ok32, n, 0, T(100, elem=1), 4096,
+                               None)
+    with pytest.raises(ValueError, match="`v`"):
+        lib.attention_split_fp32(128, 256, 128, T(128 * 128 * 4, elem=4), T(256 * 128 * 4, elem=4),
+                                 T(255 * 128 * 4, elem=4), 2, 1, T(128 * 128 * 4, elem=4), T(1 << 20, elem=1), 1 << 20,
+                                 None)
+
+
+def test_extent_of_stored_operands():
+    from mma_fragment_layouts_amd import _binding as B
+    assert B._op(3, 5, 8, B.ROW_MAJOR, 2) == ((3 - 1) * 8 + 5) * 2
+    assert B._op(3, 5, 8, B.COL_MAJOR, 2) == ((5 - 1) * 8 + 3) * 2
+    assert B._op(0, 5, 8, B.ROW_MAJOR, 2) == 0
+    assert B._extent(4, 4, 4, 4) == 64
