@@ -132,6 +132,14 @@ def _need(fn: str, **bufs) -> None:
             raise ValueError(f"{fn}: `{name}` needs {nbytes} bytes from its data pointer; the tensor holds {room}")
 
 
+def _layout_info(fn, *args) -> Optional[Tuple[int, int, int, int]]:
+    """(lanes, per_lane, rows, cols) from an info call, or None if it fails."""
+    v = [C.c_int() for _ in range(4)]
+    if fn(*args, *[C.byref(x) for x in v]) != OK:
+        return None
+    return tuple(x.value for x in v)
+
+
 def _stream(s) -> Optional[int]:
     if s is None:
         return None
@@ -229,16 +237,30 @@ def operand_matrix_offset(shape: int, operand: int, lane: int, i: int, row0: int
 
 
 def operand_load_strided(shape, operand, m, row0, col0, ld, order, frag, stream=None) -> None:
+    info = _layout_info(load().mfl_operand_info, shape, operand)
+    if info:  # an unknown shape or operand is left to the library to reject
+        lanes, per_lane, rows, cols = info
+        _need("operand_load_strided", m=(m, _op(row0 + rows, col0 + cols, ld, order, 2)),
+              frag=(frag, lanes * per_lane * 2))
     _check(load().operand_load_strided(shape, operand, _ptr(m), row0, col0, ld, order, _ptr(frag), _stream(stream)),
            "operand_load_strided")
 
 
 def acc_store_strided(shape, acc, c, row0, col0, ldc, stream=None) -> None:
+    info = _layout_info(load().mfl_acc_info, shape)
+    if info:
+        lanes, per_lane, rows, cols = info
+        _need("acc_store_strided", acc=(acc, lanes * per_lane * 4), c=(c, _extent(row0 + rows, col0 + cols, ldc, 4)))
     _check(load().acc_store_strided(shape, _ptr(acc), _ptr(c), row0, col0, ldc, _stream(stream)),
            "acc_store_strided")
 
 
 def mfma_probe(shape, dtype, a_frag, b_frag, c_in, acc, stream=None) -> None:
+    info = _layout_info(load().mfl_acc_info, shape)
+    if info:
+        lanes, per_lane, _, _ = info
+        _need("mfma_probe", a_frag=(a_frag, 64 * 8 * 2), b_frag=(b_frag, 64 * 8 * 2),
+              c_in=(c_in, lanes * per_lane * 4), acc=(acc, lanes * per_lane * 4))
     _check(load().mfma_probe(shape, dtype, _ptr(a_frag), _ptr(b_frag), _ptr(c_in), _ptr(acc), _stream(stream)),
            "mfma_probe")
 

@@ -488,3 +488,14 @@ def test_extent_of_stored_operands():
     assert B._op(3, 5, 8, B.COL_MAJOR, 2) == ((5 - 1) * 8 + 3) * 2
     assert B._op(0, 5, 8, B.ROW_MAJOR, 2) == 0
     assert B._extent(4, 4, 4, 4) == 64
+
+
+def test_undersized_probe_buffers_are_refused(lib):
+    T = _DeviceTensorStandIn
+    frag = T(64 * 8 * 2)
+    with pytest.raises(ValueError, match="`acc`"):   # 32x32x16: 16 fp32 per lane
+        lib.mfma_probe(1, lib.F16, frag, frag, None, T(64 * 4 * 4, elem=4), None)
+    with pytest.raises(ValueError, match="`frag`"):
+        lib.operand_load_strided(0, 0, T(1 << 20), 0, 0, 64, lib.ROW_MAJOR, T(64 * 8 * 2 - 2), None)
+    with pytest.raises(ValueError, match="`c`"):     # 16x16 tile at (16, 16) of an ld-32 matrix
+        lib.acc_store_strided(0, T(64 * 4 * 4, elem=4), T((31 * 32 + 31) * 4, elem=4), 16, 16, 32, None)
