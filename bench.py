@@ -94,6 +94,21 @@ def source_digest(paths):
     return h.hexdigest()
 
 
+def measured_counters():
+    """MFMA-busy and LDS counters per GEMM launch from the committed rocprofv3
+    record, or None when the kernel sources have changed since they were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+        if source_digest(rec["sources"]) != rec["source_digest"]:
+            return None
+        c = dict(rec["counters"])
+        c.pop("note", None)
+        c["source"] = "profiles/gemm_4096_bf16_counters.md"
+        return c
+    except Exception:
+        return None
+
+
 def measured_traffic():
     """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     record (scaled by a plain copy), or None when the kernel sources have changed
@@ -437,6 +452,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
+        # MFMA busy and LDS bank conflicts of this kernel from the committed counter run
+        "counters": measured_counters() if args.shape == 0 else None,
     }
     if not args.no_clock:
         log("clock under load")

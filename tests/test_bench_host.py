@@ -41,3 +41,21 @@ def test_measured_traffic_follows_the_record_digest(tmp_path, monkeypatch):
     path.write_text(json.dumps(stale))
     monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(path))
     assert bench.measured_traffic() is None
+
+
+def test_measured_counters_follow_the_record_digest(tmp_path, monkeypatch):
+    rec = json.load(open(bench.TRAFFIC_RECORD))
+    current = bench.source_digest(rec["sources"]) == rec["source_digest"]
+    got = bench.measured_counters()
+    if current:
+        assert got["lds_bank_conflict_cycles"] == 0
+        assert 0 < got["mfma_busy_under_profiler"] <= 1
+        # every MFMA op is bf16: 2 * 4096^3 flop at 512 flop per op
+        assert got["mfma_mops_bf16"] * 512 == 2 * 4096 ** 3
+    else:
+        assert got is None
+    stale = dict(rec, source_digest="0" * 64)
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(stale))
+    monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(path))
+    assert bench.measured_counters() is None
