@@ -1,0 +1,109 @@
+"""Seeded random shapes through the GEMM entry points, against the oracle.
+
+Hand-picked sizes cover each path once; random (m, n, k), operand orders,
+padded leading dimensions, element types and accumulate flags also cross the
+dispatch boundaries (64 / 128 / 256 tiles, the EDGE variants, the generic path
+for k not a multiple of 8) in combinations nobody listed.  Every case checks
+the m x n block of C against the oracle and that C's padding columns are
+untouched."""
+import numpy as np
+import pytest
+import torch
+
+import mma_fragment_layouts_amd as mfl
+from mma_fragment_layouts_amd import inputs
+from oracle import reference as R
+
+from _gpu import DT, dev32, device, host, q16, say, stream
+
+pytestmark = pytest.mark.gpu
+SENTINEL = 12345.0
+
+
+def dense_cases(count=40, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        m, n = int(rng.integers(1, 700)), int(rng.integers(1, 700))
+        # mostly multiples of 8 (fast path); every fourth case any k (generic path when k % 8 != 0)
+        k = int(rng.integers(1, 600)) if i % 4 == 3 else 8 * int(rng.integers(1, 75))
+        out.append((m, n, k, int(rng.integers(0, 2)), int(rng.integers(0, 2)), ("f16", "bf16")[int(rng.integers(0, 2))],
+                    int(rng.integers(0, 2)), int(rng.integers(0, 3)) * 8, int(rng.integers(1, 6))))
+    return out
+
+
+@pytest.mark.parametrize("case", dense_cases(), ids=lambda c: "x".join(map(str, c[:3])) + f"-o{c[3]}{c[4]}-{c[5]}-acc{c[6]}")
+def test_gemm_tile_mma_random_shape(case):
+    m, n, k, oa, ob, fmt, accumulate, pad, cpad = case
+    say("random gemm", case)
+    rng = np.random.default_rng(m * 1000003 + n * 1009 + k)
+    a = rng.uniform(-1, 1, (m, k)).astype(np.float32)
+    bt = rng.uniform(-1, 1, (n, k)).astype(np.float32)
+    sa = a if oa == mfl.ROW_MAJOR else np.ascontiguousarray(a.T)     # storage: rows x inner
+    sb = bt if ob == mfl.COL_MAJOR else np.ascontiguousarray(bt.T)
+    lda = sa.shape[1] + (-sa.shape[1]) % 8 + pad
+    ldb = sb.shape[1] + (-sb.shape[1]) % 8 + pad
+    pa = np.full((sa.shape[0], lda), np.nan, np.float32)
+    pa[:, :sa.shape[1]] = sa
+    pb = np.full((sb.shape[0], ldb), np.nan, np.float32)
+    pb[:, :sb.shape[1]] = sb
+    ldc = n + cpad
+    c0 = np.full((m, ldc), SENTINEL, np.float32)
+    c0[:, :n] = rng.standard_normal((m, n)).astype(np.float32) if accumulate else np.nan
+    c = dev32(c0)
+    mfl.gemm_tile_mma(DT[fmt], m, n, k, q16(pa, fmt), lda, oa, q16(pb, fmt), ldb, ob, c, ldc, accumulate, stream())
+    ch = host(c)
+    assert (ch[:, n:] == SENTINEL).all(), "C padding written"
+    ref = R.gemm_ref(a, bt, fmt) + (c0[:, :n].astype(np.float64) if accumulate else 0.0)
+    assert not np.isnan(ch[:, :n]).any()
+    assert R.rel_error(ch[:, :n], ref) <= 1e-5
+
+
+def split_cases(count=16, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        m, n = 8 * int(rng.integers(1, 80)), 8 * int(rng.integers(1, 80))
+        k = 8 * int(rng.integers(1, 60)) if i % 4 else int(rng.integers(1, 400))
+        out.append((m, n, k, int(rng.integers(0, 2)), int(rng.integers(0, 2)), int(rng.integers(1, 4))))
+    return out
+
+
+@pytest.mark.parametrize("case", split_cases(), ids=lambda c: "x".join(map(str, c[:3])) + f"-o{c[3]}{c[4]}-ch{c[5]}")
+def test_split_gemm_random_shape(case):
+    """Both split entry points (planes with a workspace, split on load without)
+    on the same random problem: identical bits, and within the oracle bound."""
+    m, n, k, oa, ob, chains = case
+    say("random split", case)
+    a, bt = inputs.gemm_split(m, n, k)
+    sa = a if oa == mfl.ROW_MAJOR else np.ascontiguousarray(a.T)
+    sb = bt if ob == mfl.COL_MAJOR else np.ascontiguousarray(bt.T)
+    lda = sa.shape[1] + (-sa.shape[1]) % 8 + 8
+    ldb = sb.shape[1] + (-sb.shape[1]) % 8 + 16
+    pa = np.full((sa.shape[0], lda), np.nan, np.float32)
+    pa[:, :sa.shape[1]] = sa
+    pb = np.full((sb.shape[0], ldb), np.nan, np.float32)
+    pb[:, :sb.shape[1]] = sb
+    da, db = dev32(pa), dev32(pb)
+    ldc = n + 3
+    c_load = dev32(np.full((m, ldc), SENTINEL, np.float32))
+    c_ws = dev32(np.full((m, ldc), SENTINEL, np.float32))
+    wsb = mfl.gemm_split_fp32_workspace_bytes(m, n, k, lda, oa, mfl.SPLIT, ldb, ob, mfl.SPLIT, ldc)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=device())
+    mfl.gemm_split_fp32(mfl.BF16, m, n, k, da, lda, oa, mfl.SPLIT, db, ldb, ob, mfl.SPLIT, chains, 0, c_load, ldc, 0,
+                        stream())
+    mfl.gemm_split_fp32_ws(mfl.BF16, m, n, k, da, lda, oa, mfl.SPLIT, db, ldb, ob, mfl.SPLIT, chains, 0, c_ws, ldc, 0,
+                           ws, wsb, stream())
+    hl, hw = host(c_load), host(c_ws)
+    assert (hl[:, n:] == SENTINEL).all() and (hw[:, n:] == SENTINEL).all(), "C padding written"
+    assert np.array_equal(hl[:, :n].view(np.uint32), hw[:, :n].view(np.uint32))
+    # The kernels' own (accumulation) error is measured against the exact value
+    # of the bf16 hi/lo expansion, with the bounds of the medium-size split test.
+    # The 5e-6 bound against the original fp32 operands is stated for the 4096^3
+    # workload; on a small random problem the split's representation floor alone
+    # can exceed it, so it is reported here, not asserted.
+    exp3 = R.split_expansion(a, bt, "bf16")
+    acc_err = R.rel_error(hw[:, :n], exp3)
+    print(f"accumulation error {acc_err:.3e}, against fp32 inputs {R.rel_error(hw[:, :n], R.split_ref(a, bt)):.3e}, "
+          f"split floor {R.rel_error(exp3, R.split_ref(a, bt)):.3e}")
+    assert acc_err <= (2e-6 if chains >= 2 else 2e-5)
