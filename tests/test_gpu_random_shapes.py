@@ -107,3 +107,28 @@ def test_split_gemm_random_shape(case):
     print(f"accumulation error {acc_err:.3e}, against fp32 inputs {R.rel_error(hw[:, :n], R.split_ref(a, bt)):.3e}, "
           f"split floor {R.rel_error(exp3, R.split_ref(a, bt)):.3e}")
     assert acc_err <= (2e-6 if chains >= 2 else 2e-5)
+
+
+def attention_cases(count=12, seed=5):
+    rng = np.random.default_rng(seed)
+    return [(128 * int(rng.integers(1, 9)), 128 * int(rng.integers(1, 65)), int(rng.integers(1, 3)), int(rng.integers(0, 3)))
+            for _ in range(count)]
+
+
+@pytest.mark.parametrize("case", attention_cases(), ids=lambda c: f"{c[0]}x{c[1]}-ch{c[2]}-algo{c[3]}")
+def test_attention_random_shape(case):
+    """Random query and key counts (multiples of 128) through every attention
+    algorithm: key-slice counts and per-slice chunk counts vary, odd ones
+    included; against the fp64 oracle (on the quantisation each algorithm
+    applies: K and V rounded once, or split too for algorithm 2)."""
+    nq, nk, chains, algo = case
+    say("random attention", case)
+    q, k, v = inputs.attention(nq, nk)
+    wsb = mfl.attention_workspace_bytes(nq, nk, 128, algo)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=device())
+    o = torch.full((nq, 128), np.nan, device=device())
+    mfl.attention_split_fp32(nq, nk, 128, dev32(q), dev32(k), dev32(v), chains, algo, o, ws, wsb, stream())
+    ref = R.attention_ref(q, k, v, round_kv=(algo != mfl.ATTN_FUSED_SPLIT_KV))
+    err = R.rel_error(host(o), ref)
+    print(f"attention {case}: error {err:.3e}")
+    assert err <= 5e-6
