@@ -190,6 +190,8 @@ def sclk_under_load(step, torch, seconds=1.0):
 
 
 EXTRA = ("gemm_256", "gemm_orders", "block_repeat", "split", "attention")
+# opt-in legs (not run by default)
+EXTRA_OPTIONAL = ("gemm_sizes",)
 
 
 def extra_workloads(torch, mfl, inputs, stream, which=EXTRA):
@@ -212,6 +214,8 @@ def extra_workloads(torch, mfl, inputs, stream, which=EXTRA):
         split(torch, mfl, inputs, stream, dev, out)
     if "attention" in which:
         attention(torch, mfl, inputs, stream, dev, out)
+    if "gemm_sizes" in which:
+        gemm_sizes(torch, mfl, inputs, stream, dev, q16, out)
     return out
 
 
@@ -277,6 +281,30 @@ def gemm_orders(torch, mfl, inputs, stream, dev, q16, out):
         var[label] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
         del da, db
     out["gemm_4096_variants"] = var
+
+
+def gemm_sizes(torch, mfl, inputs, stream, dev, q16, out):
+    """The bf16 GEMM (A row-major, B column-major, fp32 C, ld = n + 64) at square
+    sizes from 1024 to 8192.  The fast path covers C with 256 x 256 tiles, one
+    workgroup each: 4096^3 is one tile per compute unit, so every unit stores its
+    fp32 tile at the same moment; at 8192^3 (four tiles per unit) a tile's store
+    can overlap other units' K loops."""
+    res = {}
+    for n in (1024, 2048, 3072, 4096, 6144, 8192):
+        a, bt = inputs.gemm_dense(n, n, n)
+        ld = a.shape[1]
+        da, db = q16(a, mfl.BF16), q16(bt, mfl.BF16)
+        del a, bt
+        c = torch.empty((n, n), device=dev)
+        ms = best_of(lambda: mfl.gemm_tile_mma(mfl.BF16, n, n, n, da, ld, mfl.ROW_MAJOR, db, ld, mfl.COL_MAJOR, c, n,
+                                               0, stream), stream)
+        tf = 2 * n ** 3 / ms / 1e9
+        tiles = ((n + 255) // 256) ** 2
+        res[str(n)] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                       "tiles_per_cu": round(tiles / 256, 3)}
+        log(f"gemm {n}^3: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+        del da, db, c
+    out["gemm_bf16_sizes"] = res
 
 
 def block_repeat(torch, mfl, inputs, stream, dev, q16, out):
@@ -364,7 +392,8 @@ def main():
     p.add_argument("--shape", type=int, default=0, help="MFMA shape of the GEMM fast path (0: 16x16x32, 1: 32x32x16)")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     p.add_argument("--extra", default=",".join(EXTRA),
-                   help="comma list of the other workloads to run (" + ", ".join(EXTRA) + ")")
+                   help="comma list of the other workloads to run (" + ", ".join(EXTRA) + "; opt-in: " +
+                   ", ".join(EXTRA_OPTIONAL) + ")")
     p.add_argument("--prewarm-ms", type=float, default=100.0,
                    help="untimed back-to-back GEMM launches before the warm-up steps, in ms (clock settling)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -372,6 +401,11 @@ def main():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run 3 plain device copies of 256 MiB (reference for the HBM byte counters)")
     args = p.parse_args()
+    which = tuple(w for w in args.extra.split(",") if w)
+    unknown = [w for w in which if w not in EXTRA + EXTRA_OPTIONAL]
+    if unknown:
+        print(f"unknown --extra workloads {unknown}; choose from {EXTRA + EXTRA_OPTIONAL}", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GEMM shards by output "
               "blocks with no exchange, so N GPUs would run N independent copies.", file=sys.stderr)
@@ -468,11 +502,6 @@ def main():
         del src, dst
     if not args.no_extra:
         log("other workloads")
-        which = tuple(w for w in args.extra.split(",") if w)
-        unknown = [w for w in which if w not in EXTRA]
-        if unknown:
-            print(f"unknown --extra workloads {unknown}; choose from {EXTRA}", file=sys.stderr)
-            sys.exit(2)
         result["workloads"] = extra_workloads(torch, mfl, inputs, stream, which)
     if not args.no_cpu:
         log("cpu oracle baseline")

@@ -59,3 +59,11 @@ def test_measured_counters_follow_the_record_digest(tmp_path, monkeypatch):
     path.write_text(json.dumps(stale))
     monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(path))
     assert bench.measured_counters() is None
+
+
+def test_unknown_extra_workload_is_refused_before_any_device_work():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--extra", "gemm_sizes,nonesuch"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "nonesuch" in r.stderr and "gemm_sizes" not in r.stderr.split("choose from")[0]
+    assert r.stdout == ""
