@@ -1,8 +1,9 @@
 """Host models of the fast GEMM path's tile order, operand extents and epilogue.
 
 These run on the CPU and check the design's index arithmetic for the
-configurations the fast path launches (256 x 256 tiles with 4 x 4 waves,
-128 x 128 with 2 x 2, 64 x 64 with 2 x 1) at tile-multiple and ragged sizes:
+configurations the fast paths launch (dense GEMM: 256 x 256 tiles with 4 x 4
+waves, 128 x 128 with 2 x 2, 64 x 64 with 2 x 1; split GEMM planes kernel:
+128 x 128 with 2 x 4) at tile-multiple and ragged sizes:
 
   * the XCD-aware tile order (``tile_of`` in csrc/common.hpp) visits every
     tile of the grid exactly once;
@@ -23,8 +24,8 @@ import pytest
 
 import mma_fragment_layouts_amd as mfl
 
-# (BM, BN, WGM, WGN) of the fast path's launches
-CONFIGS = [(256, 256, 4, 4), (128, 128, 2, 2), (64, 64, 2, 1)]
+# (BM, BN, WGM, WGN): the dense fast path's launches and the split planes kernel's
+CONFIGS = [(256, 256, 4, 4), (128, 128, 2, 2), (64, 64, 2, 1), (128, 128, 2, 4)]
 RAGGED = [(4096, 4096), (4000, 4000), (1000, 520), (300, 1000), (257, 129), (64, 64), (1, 1)]
 
 
