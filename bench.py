@@ -301,7 +301,7 @@ def gemm_sizes(torch, mfl, inputs, stream, dev, q16, out):
         tf = 2 * n ** 3 / ms / 1e9
         tiles = ((n + 255) // 256) ** 2
         res[str(n)] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                       "tiles_per_cu": round(tiles / 256, 3)}
+                       "tiles_256_per_cu": round(tiles / 256, 3)}
         log(f"gemm {n}^3: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
         del da, db, c
     out["gemm_bf16_sizes"] = res

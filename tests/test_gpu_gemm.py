@@ -14,6 +14,7 @@ from _gpu import DT, dev32, device, host, q16, say, stream
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
+SENTINEL = 12345.0
 
 
 def storage(x_logical, order, ld, pad_value=np.nan):
@@ -287,3 +288,36 @@ def test_fast_path_ragged_all_orders(mnk, accumulate, fmt):
             first = out.copy()
         else:
             assert np.array_equal(out.view(np.uint32), first.view(np.uint32)), (oa, ob)
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+@pytest.mark.parametrize("accumulate", [0, 1])
+def test_wave_quantisation_split_6144(shape, accumulate):
+    """6144^3 (576 tiles of 256 x 256: two full rounds on 256 CUs and a quarter
+    round) runs as two launches: rows 0-5119 with 256-tiles, rows 5120-6143 with
+    128-tiles.  Row blocks of both regions, and the block across the boundary,
+    recomputed by standalone calls on those rows alone, must match bit for bit
+    (the tile size does not change an element's MFMA sequence); sampled rows of
+    both regions against the oracle; the padding of C untouched."""
+    n, ldc = 6144, 6144 + 4
+    a, bt = inputs.gemm_dense(n, n, n)
+    ld = a.shape[1]
+    say("quantisation split 6144^3", shape, accumulate)
+    da, db = q16(a, "bf16"), q16(bt, "bf16")
+    rng = np.random.default_rng(21)
+    c0 = np.full((n, ldc), SENTINEL, np.float32)
+    c0[:, :n] = rng.standard_normal((n, n)).astype(np.float32) if accumulate else np.nan
+    c = dev32(c0)
+    mfl.gemm_tile_mma_shape(shape, mfl.BF16, n, n, n, da, ld, mfl.ROW_MAJOR, db, ld, mfl.COL_MAJOR, c, ldc,
+                            accumulate, stream())
+    ch = host(c)
+    assert (ch[:, n:] == SENTINEL).all(), "C padding written"
+    assert not np.isnan(ch[:, :n]).any()
+    for r0, rows in ((0, 256), (4992, 256), (5888, 256)):    # main region, across the boundary, rest
+        part = dev32(c0[r0:r0 + rows])
+        mfl.gemm_tile_mma_shape(shape, mfl.BF16, rows, n, n, da[r0:], ld, mfl.ROW_MAJOR, db, ld, mfl.COL_MAJOR,
+                                part, ldc, accumulate, stream())
+        assert np.array_equal(host(part)[:, :n].view(np.uint32), ch[r0:r0 + rows, :n].view(np.uint32)), r0
+    sample = np.concatenate([rng.choice(5120, 12, replace=False), 5120 + rng.choice(1024, 12, replace=False)])
+    ref = R.gemm_ref(a[sample, :n], bt[:, :n], "bf16") + (c0[sample, :n].astype(np.float64) if accumulate else 0.0)
+    assert R.rel_error(ch[sample, :n], ref) <= TOL
