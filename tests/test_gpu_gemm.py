@@ -292,32 +292,35 @@ def test_fast_path_ragged_all_orders(mnk, accumulate, fmt):
 
 @pytest.mark.parametrize("shape", [0, 1])
 @pytest.mark.parametrize("accumulate", [0, 1])
-def test_wave_quantisation_split_6144(shape, accumulate):
-    """6144^3 (576 tiles of 256 x 256: two full rounds on 256 CUs and a quarter
-    round) runs as two launches: rows 0-5119 with 256-tiles, rows 5120-6143 with
-    128-tiles.  Row blocks of both regions, and the block across the boundary,
-    recomputed by standalone calls on those rows alone, must match bit for bit
-    (the tile size does not change an element's MFMA sequence); sampled rows of
-    both regions against the oracle; the padding of C untouched."""
-    n, ldc = 6144, 6144 + 4
-    a, bt = inputs.gemm_dense(n, n, n)
+@pytest.mark.parametrize("m,n,k", [(6144, 6144, 6144), (6000, 6100, 2000)])
+def test_wave_quantisation_split(m, n, k, shape, accumulate):
+    """Sizes with two full rounds of 256 x 256 tiles on 256 CUs and a partial
+    one run as two launches: rows 0-5119 with 256-tiles, the rest with
+    128-tiles (6144^3: 576 tiles; 6000 x 6100 x 2000: 24 x 24 tiles, ragged M,
+    N and a K tail, so both launches run their EDGE variants).  Row blocks of
+    both regions and the block across the boundary, recomputed by standalone
+    calls on those rows alone, must match bit for bit (the tile size does not
+    change an element's MFMA sequence); sampled rows of both regions against
+    the oracle; the padding of C untouched."""
+    ldc = n + 4
+    a, bt = inputs.gemm_dense(m, n, k)
     ld = a.shape[1]
-    say("quantisation split 6144^3", shape, accumulate)
+    say("quantisation split", m, n, k, shape, accumulate)
     da, db = q16(a, "bf16"), q16(bt, "bf16")
     rng = np.random.default_rng(21)
-    c0 = np.full((n, ldc), SENTINEL, np.float32)
-    c0[:, :n] = rng.standard_normal((n, n)).astype(np.float32) if accumulate else np.nan
+    c0 = np.full((m, ldc), SENTINEL, np.float32)
+    c0[:, :n] = rng.standard_normal((m, n)).astype(np.float32) if accumulate else np.nan
     c = dev32(c0)
-    mfl.gemm_tile_mma_shape(shape, mfl.BF16, n, n, n, da, ld, mfl.ROW_MAJOR, db, ld, mfl.COL_MAJOR, c, ldc,
+    mfl.gemm_tile_mma_shape(shape, mfl.BF16, m, n, k, da, ld, mfl.ROW_MAJOR, db, ld, mfl.COL_MAJOR, c, ldc,
                             accumulate, stream())
     ch = host(c)
     assert (ch[:, n:] == SENTINEL).all(), "C padding written"
     assert not np.isnan(ch[:, :n]).any()
-    for r0, rows in ((0, 256), (4992, 256), (5888, 256)):    # main region, across the boundary, rest
+    for r0, rows in ((0, 256), (4992, 256), (m - 200, 200)):    # main region, across the boundary, rest
         part = dev32(c0[r0:r0 + rows])
-        mfl.gemm_tile_mma_shape(shape, mfl.BF16, rows, n, n, da[r0:], ld, mfl.ROW_MAJOR, db, ld, mfl.COL_MAJOR,
+        mfl.gemm_tile_mma_shape(shape, mfl.BF16, rows, n, k, da[r0:], ld, mfl.ROW_MAJOR, db, ld, mfl.COL_MAJOR,
                                 part, ldc, accumulate, stream())
         assert np.array_equal(host(part)[:, :n].view(np.uint32), ch[r0:r0 + rows, :n].view(np.uint32)), r0
-    sample = np.concatenate([rng.choice(5120, 12, replace=False), 5120 + rng.choice(1024, 12, replace=False)])
-    ref = R.gemm_ref(a[sample, :n], bt[:, :n], "bf16") + (c0[sample, :n].astype(np.float64) if accumulate else 0.0)
+    sample = np.concatenate([rng.choice(5120, 12, replace=False), 5120 + rng.choice(m - 5120, 12, replace=False)])
+    ref = R.gemm_ref(a[sample, :k], bt[:, :k], "bf16") + (c0[sample, :n].astype(np.float64) if accumulate else 0.0)
     assert R.rel_error(ch[sample, :n], ref) <= TOL
