@@ -40,7 +40,9 @@ def eager_noise(shape):
 
 @pytest.mark.parametrize("mnk,orders", [((2048, 1536, 1024), (mfl.ROW_MAJOR, mfl.COL_MAJOR)),
                                         ((1000, 520, 200), (mfl.COL_MAJOR, mfl.ROW_MAJOR)),
-                                        ((256, 256, 256), (mfl.ROW_MAJOR, mfl.COL_MAJOR))])
+                                        ((256, 256, 256), (mfl.ROW_MAJOR, mfl.COL_MAJOR)),
+                                        # 24 x 24 tiles of 256: the row split, two launches per call
+                                        ((6144, 6144, 1024), (mfl.ROW_MAJOR, mfl.COL_MAJOR))])
 def test_graph_gemm_tile_mma(mnk, orders):
     m, n, k = mnk
     oa, ob = orders
