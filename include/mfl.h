@@ -204,10 +204,10 @@ MFL_API int split_fp32(int dtype, const float *x, void *hi, void *lo, int64_t n,
  * outside the m x n block of C, padding included, is written).  A
  * column-major A or row-major B is staged K-major in LDS and read with the
  * gfx950 transpose read, with results bit-identical to the K-contiguous
- * orders.  With K-contiguous operands, a size whose 256 x 256 tiles fill at
- * least two whole rounds of one tile per compute unit plus a partial one runs
- * as two launches on the stream, split by rows: whole rounds of 256-tiles,
- * then one round of 128-tiles.  The bits are the same as with one launch.
+ * orders.  A size whose 256 x 256 tiles fill at least two whole rounds of
+ * one tile per compute unit plus a partial one runs as two launches on the
+ * stream, split by rows: whole rounds of 256-tiles, then one round of
+ * 128-tiles.  The bits are the same as with one launch.
  * Other sizes take the generic path.  Reads never go past the
  * minimum storage of an operand, (rows - 1) * ld + the inner extent. */
 MFL_API int gemm_tile_mma(int dtype, int64_t m, int64_t n, int64_t k,

@@ -205,8 +205,9 @@ static bool fast_fits(bool kmajor, int64_t ld, int64_t K) {
 // rounds of 256-tiles and the remaining rows as a second launch of 128 x 128
 // tiles (two workgroups per CU), which must fit one round (at most 512 tiles).
 // m1 is one tile-row below the most that fits the full rounds (one more if the
-// rest would not fit one round); measured on K-contiguous operands: 6144^3
-// +9 %, 7168^3 +9 %, 10240 x 4096 x 4096 +4 %.  Each output element sees the
+// rest would not fit one round).  Measured, K-contiguous operands: 6144^3
+// +9 %, 7168^3 +9 %, 10240 x 4096 x 4096 +4 %; k-major A and/or B: 6144^3
+// +7-9 %, 7168^3 +2-5 %.  Each output element sees the
 // same MFMA sequence whatever the tile size, so the two launches give the same
 // bits as one.  Returns m1, or 0 for a single launch.
 static int quantisation_split_rows(int M, int N) {
@@ -230,17 +231,16 @@ static int dispatch_fast(int shape, const void* a, int64_t lda, const void* b, i
   // are not tile multiples run the EDGE variant of the same kernel.
   const auto count = [&](int t) { return (int64_t)((M + t - 1) / t) * ((N + t - 1) / t); };
   const bool s32 = shape == MFL_MFMA_32X32X16;
-  if constexpr (!AKM && !BKM) {
-    if (const int m1 = quantisation_split_rows(M, N)) {
-      const int M1 = 256 * m1;
-      const auto a2 = (const uint16_t*)a + (int64_t)M1 * lda;  // row-major A: rows M1.. start M1 rows in
-      float* c2 = c + (int64_t)M1 * ldc;
-      const int r = s32 ? launch_fast<256, 256, 4, 4, 1, DT, false, false>(a, lda, b, ldb, c, ldc, M1, N, K, accumulate, s)
-                        : launch_fast<256, 256, 4, 4, 0, DT, false, false>(a, lda, b, ldb, c, ldc, M1, N, K, accumulate, s);
-      if (r != MFL_OK) return r;
-      return s32 ? launch_fast<128, 128, 2, 2, 1, DT, false, false>(a2, lda, b, ldb, c2, ldc, M - M1, N, K, accumulate, s)
-                 : launch_fast<128, 128, 2, 2, 0, DT, false, false>(a2, lda, b, ldb, c2, ldc, M - M1, N, K, accumulate, s);
-    }
+  if (const int m1 = quantisation_split_rows(M, N)) {
+    const int M1 = 256 * m1;
+    // rows M1.. of A: M1 rows in (row-major) or M1 elements in (column-major)
+    const auto a2 = (const uint16_t*)a + (AKM ? (int64_t)M1 : (int64_t)M1 * lda);
+    float* c2 = c + (int64_t)M1 * ldc;
+    const int r = s32 ? launch_fast<256, 256, 4, 4, 1, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M1, N, K, accumulate, s)
+                      : launch_fast<256, 256, 4, 4, 0, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M1, N, K, accumulate, s);
+    if (r != MFL_OK) return r;
+    return s32 ? launch_fast<128, 128, 2, 2, 1, DT, AKM, BKM>(a2, lda, b, ldb, c2, ldc, M - M1, N, K, accumulate, s)
+               : launch_fast<128, 128, 2, 2, 0, DT, AKM, BKM>(a2, lda, b, ldb, c2, ldc, M - M1, N, K, accumulate, s);
   }
   if (count(256) >= 128)
     return s32 ? launch_fast<256, 256, 4, 4, 1, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)

@@ -324,3 +324,32 @@ def test_wave_quantisation_split(m, n, k, shape, accumulate):
     sample = np.concatenate([rng.choice(5120, 12, replace=False), 5120 + rng.choice(m - 5120, 12, replace=False)])
     ref = R.gemm_ref(a[sample, :k], bt[:, :k], "bf16") + (c0[sample, :n].astype(np.float64) if accumulate else 0.0)
     assert R.rel_error(ch[sample, :n], ref) <= TOL
+
+
+@pytest.mark.parametrize("oa,ob", [(mfl.COL_MAJOR, mfl.COL_MAJOR), (mfl.ROW_MAJOR, mfl.ROW_MAJOR),
+                                   (mfl.COL_MAJOR, mfl.ROW_MAJOR)])
+def test_wave_quantisation_split_k_major(oa, ob):
+    """The row split with k-major operands (column-major A: the second launch
+    starts M1 elements in; row-major B): 6144 x 6144 x 2048, bit-identical to
+    the K-contiguous order (same MFMA sequence per element) and, per row
+    block, to standalone calls on those rows."""
+    m = n = 6144
+    k = 2048
+    a, bt = inputs.gemm_dense(m, n, k)
+    a, bt = a[:, :k], bt[:, :k]
+    say("quantisation split k-major", oa, ob)
+    sa = a if oa == mfl.ROW_MAJOR else np.ascontiguousarray(a.T)      # storage: rows x inner
+    sb = bt if ob == mfl.COL_MAJOR else np.ascontiguousarray(bt.T)
+    da, db = q16(sa, "bf16"), q16(sb, "bf16")
+    lda, ldb = sa.shape[1], sb.shape[1]
+    c_ref = torch.full((m, n), np.nan, device=device())
+    mfl.gemm_tile_mma(mfl.BF16, m, n, k, q16(a, "bf16"), k, mfl.ROW_MAJOR, q16(bt, "bf16"), k, mfl.COL_MAJOR, c_ref,
+                      n, 0, stream())
+    c = torch.full((m, n), np.nan, device=device())
+    mfl.gemm_tile_mma(mfl.BF16, m, n, k, da, lda, oa, db, ldb, ob, c, n, 0, stream())
+    assert torch.equal(c, c_ref)
+    for r0 in (0, 4992, 5888):
+        part = torch.full((256, n), np.nan, device=device())
+        sub_a = da[r0:] if oa == mfl.ROW_MAJOR else da[:, r0:]         # rows r0.. of A
+        mfl.gemm_tile_mma(mfl.BF16, 256, n, k, sub_a, lda, oa, db, ldb, ob, part, n, 0, stream())
+        assert torch.equal(part, c[r0:r0 + 256]), r0
