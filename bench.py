@@ -78,48 +78,116 @@ def best_of(fn, stream, warm=3, rounds=3, per=20, settle_ms=30.0):
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_4096_bf16_traffic.json")
+# The headline kernel: mangled name in the code object, and as the profiler names it.
+HEADLINE_SYMBOL = "gemm_fast_kernelILi256ELi256ELi4ELi4ELi0ELi1ELi2ELb0ELb0ELb0E"
+HEADLINE_PROFILED = "gemm_fast_kernel<256, 256, 4, 4, 0, 1, 2, false, false, false>"
 
 
-def source_digest(paths):
-    """sha256 of the given sources with C/C++ comments and whitespace removed, so
-    that edits of comments alone do not count as a kernel change."""
-    import hashlib
-    import re
-    h = hashlib.sha256()
-    for src in paths:
-        text = open(os.path.join(ROOT, src)).read()
-        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", " ", text)
-        h.update(" ".join(text.split()).encode())
-    return h.hexdigest()
-
-
-def measured_counters():
-    """MFMA-busy and LDS counters per GEMM launch from the committed rocprofv3
-    record, or None when the kernel sources have changed since they were taken."""
+def headline_digest():
+    """sha256 of the headline kernel's gfx950 instructions and descriptor in the
+    library that is built now (None if the library cannot be read)."""
+    from mma_fragment_layouts_amd import codeobj, library_path
     try:
-        rec = json.load(open(TRAFFIC_RECORD))
-        if source_digest(rec["sources"]) != rec["source_digest"]:
-            return None
-        c = dict(rec["counters"])
-        c.pop("note", None)
-        c["source"] = "profiles/gemm_4096_bf16_counters.md"
-        return c
+        return codeobj.kernel_digest(library_path(), HEADLINE_SYMBOL)[1]
     except Exception:
         return None
 
 
-def measured_traffic():
-    """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    record (scaled by a plain copy), or None when the kernel sources have changed
-    since the counters were taken."""
+def counter_record():
+    """The committed rocprofv3 record of the headline kernel, or None when it
+    was taken on other machine code than the library built now (the record
+    stores the digest of the kernel it measured; nothing re-keys it by hand)."""
     try:
         rec = json.load(open(TRAFFIC_RECORD))
-        if source_digest(rec["sources"]) != rec["source_digest"]:
-            return None
-        return int(rec["read_bytes"] + rec["write_bytes"])
     except Exception:
         return None
+    d = headline_digest()
+    return rec if d is not None and rec.get("code_digest") == d else None
+
+
+def measured_counters(rec):
+    """MFMA-busy and LDS counters per GEMM launch from the record."""
+    if rec is None:
+        return None
+    c = dict(rec["counters"])
+    c.pop("note", None)
+    c["source"] = "profiles/gemm_4096_bf16_counters.md"
+    return c
+
+
+def measured_traffic(rec):
+    """HBM bytes per GEMM launch (FETCH_SIZE and WRITE_SIZE scaled by a plain copy)."""
+    return None if rec is None else int(rec["read_bytes"] + rec["write_bytes"])
+
+
+def _counter_rows(directory):
+    """{kernel name: {dispatch id: {counter: value}}} from a rocprofv3 --pmc run."""
+    import csv
+    import glob
+    rows = {}
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            rows.setdefault(r["Kernel_Name"], {}).setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = \
+                float(r["Counter_Value"])
+    return rows
+
+
+def record_counters(dir_a, dir_f, dir_w, last, commands):
+    """Write the counter record of the headline kernel from three rocprofv3
+    --pmc runs of this benchmark (group A: MFMA busy, LDS; FETCH_SIZE; WRITE_SIZE,
+    the last two with --copy-calibration).  Per-dispatch values are averaged
+    over the last `last` dispatches of the kernel (warm-up and timed steps);
+    the byte counters are scaled by what they read for the 256 MiB copies.
+    The record carries the digest of the kernel in the library built now, which
+    must be the library the runs used."""
+    def per_dispatch(directory, kernel, counters, n):
+        rows = [v for k, v in _counter_rows(directory).items() if kernel in k]
+        disp = sorted((i, c) for r in rows for i, c in r.items())
+        if len(disp) < n:
+            raise SystemExit(f"{directory}: {len(disp)} dispatches of {kernel}, need {n}")
+        take = [c for _, c in disp[-n:]]
+        return {name: sum(c[name] for c in take) / n for name in counters}
+
+    a = per_dispatch(dir_a, HEADLINE_PROFILED, ["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE",
+                                                "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS",
+                                                "SQ_INSTS_VALU_MFMA_MOPS_BF16"], last)
+    f = per_dispatch(dir_f, HEADLINE_PROFILED, ["FETCH_SIZE"], last)["FETCH_SIZE"]
+    w = per_dispatch(dir_w, HEADLINE_PROFILED, ["WRITE_SIZE"], last)["WRITE_SIZE"]
+    cf = per_dispatch(dir_f, "copyBuffer", ["FETCH_SIZE"], 3)["FETCH_SIZE"]
+    cw = per_dispatch(dir_w, "copyBuffer", ["WRITE_SIZE"], 3)["WRITE_SIZE"]
+    copy_bytes = 256 << 20
+    ff, fw = copy_bytes / 1024 / cf, copy_bytes / 1024 / cw
+    gui_per_xcd = a["GRBM_GUI_ACTIVE"] / 8
+    digest = headline_digest()
+    if digest is None:
+        raise SystemExit("cannot read the headline kernel from the built library")
+    rec = {
+        "kernel": HEADLINE_PROFILED,
+        "kernel_symbol": HEADLINE_SYMBOL,
+        "workload": "M=N=K=4096 bf16, lda=ldb=4160, ldc=4096",
+        "code_digest": digest,
+        "digest": "sha256 of the kernel's gfx950 instructions and descriptor in lib/libmfl.so "
+                  "(mma_fragment_layouts_amd/codeobj.py)",
+        "commands": commands,
+        "dispatches_averaged": last,
+        "fetch_size_kib_raw": round(f, 2), "write_size_kib_raw": round(w, 2),
+        "copy_fetch_kib_raw": round(cf, 2), "copy_write_kib_raw": round(cw, 2), "copy_bytes": copy_bytes,
+        "fetch_scale": round(ff, 4), "write_scale": round(fw, 4),
+        "read_bytes": int(round(f * 1024 * ff)), "write_bytes": int(round(w * 1024 * fw)),
+        "counters": {
+            "mfma_busy_under_profiler": round(a["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui_per_xcd * 1024), 4),
+            "lds_bank_conflict_cycles": int(a["SQ_LDS_BANK_CONFLICT"]),
+            "lds_active_cycles": int(a["SQ_LDS_IDX_ACTIVE"]),
+            "mfma_mops_bf16": int(a["SQ_INSTS_VALU_MFMA_MOPS_BF16"]),
+            "lds_instructions": int(a["SQ_INSTS_LDS"]),
+            "gui_active_cycles_per_xcd": int(gui_per_xcd),
+            "note": "per dispatch; under the profiler every dispatch is serialised with a counter read-out, "
+                    "so MFMA busy is below the timed run's"},
+    }
+    with open(TRAFFIC_RECORD, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec, indent=1))
 
 
 def cpu_model():
@@ -187,6 +255,19 @@ def sclk_under_load(step, torch, seconds=1.0):
         torch.cuda.synchronize()
     th.join()
     return found.get("mhz")
+
+
+def mfma_ceiling(torch, mfl, stream, iters=512):
+    """What the matrix cores sustain with nothing else running: the library's
+    mfma_rate_probe (16 independent bf16 16x16x32 chains per wave, hashed operand
+    values, no memory or LDS traffic), timed like the other workloads."""
+    dev = torch.device("cuda:0")
+    out = torch.empty((mfl.RATE_PROBE_OUTPUTS,), device=dev)
+    ms = best_of(lambda: mfl.mfma_rate_probe(mfl.BF16, iters, 0x9E3779B9, out, stream), stream, per=10)
+    tf = mfl.mfma_rate_flops(iters) / ms / 1e9
+    return {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "probe": f"mfma_rate_probe: {mfl.RATE_PROBE_OUTPUTS // 64} waves x {iters} x 16 bf16 16x16x32 MFMA, "
+                     "no memory traffic"}
 
 
 EXTRA = ("gemm_256", "gemm_orders", "block_repeat", "split", "attention")
@@ -364,24 +445,32 @@ def split(torch, mfl, inputs, stream, dev, out):
 
 
 def attention(torch, mfl, inputs, stream, dev, out):
-    """Attention pair 2048 x 32768 x 128, both algorithms, 1 and 2 chains."""
-    q, k, v = inputs.attention()
-    dq, dk, dv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
-    o = torch.empty((2048, 128), device=dev)
-    att = {}
-    for algo, aname in ((mfl.ATTN_MATERIALISED, "materialised"), (mfl.ATTN_FUSED, "fused"),
-                        (mfl.ATTN_FUSED_SPLIT_KV, "fused_split_kv")):
-        wsb = mfl.attention_workspace_bytes(2048, 32768, 128, algo)
-        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-        nprod = 3 if algo == mfl.ATTN_FUSED_SPLIT_KV else 2   # products per GEMM: hh, hl (, lh)
-        for chains in (1, 2):
-            ms = best_of(lambda: mfl.attention_split_fp32(2048, 32768, 128, dq, dk, dv, chains, algo, o, ws, wsb,
-                                                          stream), stream, rounds=2, per=5)
-            mf = 2 * nprod * 2 * 2048 * 32768 * 128 / ms / 1e9   # 2 GEMMs x nprod products
-            att[f"{aname}_chains{chains}"] = {"ms": round(ms, 4), "mfma_tflops": round(mf, 1),
-                                              "frac_mfma_peak": round(mf / PEAK_BF16_TFLOPS, 4)}
-        del ws
-    out["attention_2048x32768"] = att
+    """Attention pair 2048 x nk x 128, all three algorithms, 1 and 2 chains, at the
+    workload's 32,768 keys; and the fused and materialised algorithms at the
+    other contexts of Strata PR #800's "Numbers" table, 8,192 and 131,072 keys."""
+    for nk, algos, key in ((32768, ((mfl.ATTN_MATERIALISED, "materialised"), (mfl.ATTN_FUSED, "fused"),
+                                     (mfl.ATTN_FUSED_SPLIT_KV, "fused_split_kv")), "attention_2048x32768"),
+                           (8192, ((mfl.ATTN_MATERIALISED, "materialised"), (mfl.ATTN_FUSED, "fused")),
+                            "attention_2048x8192"),
+                           (131072, ((mfl.ATTN_MATERIALISED, "materialised"), (mfl.ATTN_FUSED, "fused")),
+                            "attention_2048x131072")):
+        q, k, v = inputs.attention(2048, nk)
+        dq, dk, dv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+        o = torch.empty((2048, 128), device=dev)
+        att = {}
+        for algo, aname in algos:
+            wsb = mfl.attention_workspace_bytes(2048, nk, 128, algo)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+            nprod = 3 if algo == mfl.ATTN_FUSED_SPLIT_KV else 2   # products per GEMM: hh, hl (, lh)
+            for chains in (1, 2):
+                ms = best_of(lambda: mfl.attention_split_fp32(2048, nk, 128, dq, dk, dv, chains, algo, o, ws, wsb,
+                                                              stream), stream, rounds=2, per=5)
+                mf = 2 * nprod * 2 * 2048 * nk * 128 / ms / 1e9   # 2 GEMMs x nprod products
+                att[f"{aname}_chains{chains}"] = {"ms": round(ms, 4), "mfma_tflops": round(mf, 1),
+                                                  "frac_mfma_peak": round(mf / PEAK_BF16_TFLOPS, 4)}
+            del ws
+        out[key] = att
+        del dq, dk, dv, o
 
 
 def main():
@@ -398,9 +487,18 @@ def main():
                    help="untimed back-to-back GEMM launches before the warm-up steps, in ms (clock settling)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-clock", action="store_true", help="skip the SCLK reading under load")
+    p.add_argument("--no-ceiling", action="store_true", help="skip the MFMA-rate ceiling measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run 3 plain device copies of 256 MiB (reference for the HBM byte counters)")
+    p.add_argument("--record-counters", nargs=3, metavar=("PMC_A_DIR", "FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: write profiles/gemm_4096_bf16_traffic.json from three rocprofv3 --pmc runs "
+                        "of this benchmark (see profiles/gemm_4096_bf16_counters.md) and exit")
+    p.add_argument("--record-last", type=int, default=7, help="dispatches averaged by --record-counters")
+    p.add_argument("--record-commands", default="", help="the rocprofv3 commands, stored in the record")
     args = p.parse_args()
+    if args.record_counters:
+        record_counters(*args.record_counters, last=args.record_last, commands=args.record_commands)
+        return
     which = tuple(w for w in args.extra.split(",") if w)
     unknown = [w for w in which if w not in EXTRA + EXTRA_OPTIONAL]
     if unknown:
@@ -464,6 +562,7 @@ def main():
     value = flops * args.steps / wall / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     log(f"{value:.1f} TFLOP/s wall, {achieved:.1f} TFLOP/s by events, {kernel_ms * 1e3:.1f} us/launch")
+    rec = counter_record() if args.shape == 0 else None
 
     result = {
         "metric": "GEMM TFLOP/s (bf16/fp16->fp32, 4096^3) and % of MI355X MFMA peak",
@@ -484,14 +583,25 @@ def main():
                    "mfma": "16x16x32" if args.shape == 0 else "32x32x16", "tile": "256x256x64, 16 waves (64x64 each)",
                    "prewarm_ms": args.prewarm_ms},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(rec),
                      "kernel_us": round(kernel_ms * 1e3, 2)},
         # MFMA busy and LDS bank conflicts of this kernel from the committed counter run
-        "counters": measured_counters() if args.shape == 0 else None,
+        "counters": measured_counters(rec) if args.shape == 0 else None,
     }
     if not args.no_clock:
         log("clock under load")
-        result["roofline"]["sclk_mhz_under_load"] = sclk_under_load(step, torch)
+        mhz = sclk_under_load(step, torch)
+        result["roofline"]["sclk_mhz_under_load"] = mhz
+        if mhz:
+            # the same 4096 flop/clock/CU at the clock the chip held under this load
+            at_clk = 256 * 4096 * mhz * 1e6 / 1e12
+            result["roofline"]["peak_at_sclk"] = round(at_clk, 1)
+            result["roofline"]["frac_at_sclk"] = round(achieved / at_clk, 4)
+    if not args.no_ceiling:
+        log("mfma ceiling")
+        ceil = mfma_ceiling(torch, mfl, stream)
+        result["roofline"]["mfma_ceiling"] = ceil
+        result["roofline"]["frac_of_ceiling"] = round(achieved / ceil["tflops"], 4)
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

@@ -181,6 +181,23 @@ MFL_API int acc_store_strided(int shape, const float *acc, float *c, int64_t row
 MFL_API int mfma_probe(int shape, int dtype, const void *a_frag, const void *b_frag, const float *c_in,
                        float *acc, void *stream);
 
+/* MFMA rate microbenchmark (device): the ceiling a GEMM's MFMA rate is measured
+ * against.  The pages time their kernels against a published peak (Warp issue
+ * #1965, "Spike": a stated TF32 peak beside measured rates); the published
+ * MI355X figure assumes a 2.4 GHz clock that the chip does not hold under
+ * matrix load, so this call measures what the matrix cores sustain with no
+ * memory or vector work: MFL_RATE_PROBE_OUTPUTS / 64 waves (eight 4-wave
+ * workgroups per compute unit), each issuing `iters` rounds of 16 independent
+ * v_mfma_f32_16x16x32 of `dtype` (MFL_F16 or MFL_BF16).  Work per call:
+ * MFL_RATE_PROBE_OUTPUTS / 64 * iters * 16 * 16384 flop.  Operands: seed 0 sets
+ * every operand to 1.0 (then out[t] = 480 + 2048 * iters exactly while that
+ * stays below 2^24); any other seed gives per-lane values in [1, 2) from a hash
+ * of (lane, seed).  out (device, fp32, 4-byte aligned) receives
+ * MFL_RATE_PROBE_OUTPUTS values, one per thread: the sum of its accumulators.
+ * MFL_EINVAL on an unknown dtype, iters < 0 or a NULL / misaligned out. */
+#define MFL_RATE_PROBE_OUTPUTS (2048 * 256)
+MFL_API int mfma_rate_probe(int dtype, int iters, uint32_t seed, float *out, void *stream);
+
 /* Round n fp32 values to `dtype` (round-to-nearest-even; NaN stays NaN,
  * overflow gives +-inf).  out receives n 16-bit values.  Tensor-core layout
  * explainer, paragraph on mixed precision: conversion changes the values that

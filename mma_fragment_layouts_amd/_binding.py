@@ -45,6 +45,7 @@ _SIGNATURES = {
     "operand_load_strided": (_i32, [_i32, _i32, _vp, _i64, _i64, _i64, _i32, _vp, _vp]),
     "acc_store_strided": (_i32, [_i32, _vp, _vp, _i64, _i64, _i64, _vp]),
     "mfma_probe": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "mfma_rate_probe": (_i32, [_i32, _i32, C.c_uint32, _vp, _vp]),
     "quantize_fp32": (_i32, [_i32, _vp, _vp, _i64, _vp]),
     "split_fp32": (_i32, [_i32, _vp, _vp, _vp, _i64, _vp]),
     "gemm_tile_mma": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _vp, _i64, _i32, _vp]),
@@ -263,6 +264,19 @@ def mfma_probe(shape, dtype, a_frag, b_frag, c_in, acc, stream=None) -> None:
               c_in=(c_in, lanes * per_lane * 4), acc=(acc, lanes * per_lane * 4))
     _check(load().mfma_probe(shape, dtype, _ptr(a_frag), _ptr(b_frag), _ptr(c_in), _ptr(acc), _stream(stream)),
            "mfma_probe")
+
+
+RATE_PROBE_OUTPUTS = 2048 * 256   # MFL_RATE_PROBE_OUTPUTS
+
+
+def mfma_rate_flops(iters: int) -> float:
+    """Floating-point operations of one mfma_rate_probe call."""
+    return RATE_PROBE_OUTPUTS // 64 * iters * 16 * 16384.0
+
+
+def mfma_rate_probe(dtype, iters, seed, out, stream=None) -> None:
+    _need("mfma_rate_probe", out=(out, RATE_PROBE_OUTPUTS * 4))
+    _check(load().mfma_rate_probe(dtype, iters, seed, _ptr(out), _stream(stream)), "mfma_rate_probe")
 
 
 def quantize_fp32(dtype, x, out, n, stream=None) -> None:
