@@ -9,7 +9,9 @@
  *    before any HIP call is made, so a rejected call has no side effect.
  *  - Matrix pointers are DEVICE pointers owned by the caller.  The library never
  *    allocates or frees device memory; scratch space, where an operation needs
- *    it, is a caller-provided workspace whose size a query function returns.
+ *    it, is a caller-provided workspace whose size a query function returns
+ *    (one variant, attention_split_fp32_static, uses a static device array of
+ *    the library instead).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Device calls only enqueue work and return; results are ready when the
  *    stream is synchronised.  Calls on one stream are ordered; calls on
@@ -52,7 +54,8 @@ typedef enum {
   MFL_EINVAL = -1,        /* bad argument: null pointer, out-of-range index, bad ld/alignment */
   MFL_EOVERFLOW = -2,     /* the result would not fit (the cuda-oxide page's "None on overflow") */
   MFL_EUNSUPPORTED = -3,  /* valid request this build does not implement */
-  MFL_EHIP = -4           /* a HIP launch failed (hipGetLastError after enqueue) */
+  MFL_EHIP = -4,          /* a HIP launch failed (hipGetLastError after enqueue) */
+  MFL_ESCRATCH = -5       /* the call needs more than the library's static scratch array holds */
 } mfl_status;
 
 typedef enum { MFL_MFMA_16X16X32 = 0, MFL_MFMA_32X32X16 = 1 } mfl_shape;
@@ -340,6 +343,25 @@ MFL_API int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int alg
 MFL_API int attention_split_fp32(int64_t nq, int64_t nk, int64_t d, const float *q, const float *k,
                                  const float *v, int chains, int algo, float *o, void *workspace,
                                  int64_t workspace_bytes, void *stream);
+
+/* attention_split_fp32 without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture that may not call
+ * hipMalloc, serving loops that forbid allocation, harnesses without an
+ * allocator): same arguments, algorithms, kernels and results (bit for bit) as
+ * attention_split_fp32, and the call allocates nothing.  The workspace is a
+ * static device array of MFL_ATTN_STATIC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends; the first call on a device
+ * looks up that device's copy (hipGetSymbolAddress), later calls reuse it.
+ * Calls whose attention_workspace_bytes exceeds the array return MFL_ESCRATCH
+ * before any device work: 64 MiB holds algo 1 (32.3 MiB) and algo 2 (48.3 MiB)
+ * at 2048 queries x 32768 keys, while algo 0, which materialises the nq x nk
+ * scores, fits only small sizes.  Every call on a GPU shares that GPU's array, and the
+ * array keeps the last call's contents (no call relies on them: every step
+ * writes its part of the workspace before reading it); calls that overlap on
+ * one GPU — on different streams, or from different host threads — race. */
+#define MFL_ATTN_STATIC_SCRATCH_BYTES ((int64_t)64 << 20)
+MFL_API int attention_split_fp32_static(int64_t nq, int64_t nk, int64_t d, const float *q, const float *k,
+                                        const float *v, int chains, int algo, float *o, void *stream);
 
 #ifdef __cplusplus
 }

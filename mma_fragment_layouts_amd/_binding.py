@@ -18,7 +18,7 @@ from typing import Optional, Tuple
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmfl.so")
 
 # enums (values fixed by include/mfl.h)
-OK, EINVAL, EOVERFLOW, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
+OK, EINVAL, EOVERFLOW, EUNSUPPORTED, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5
 MFMA_16X16X32, MFMA_32X32X16 = 0, 1
 F16, BF16 = 0, 1
 ROW_MAJOR, COL_MAJOR = 0, 1
@@ -60,6 +60,7 @@ _SIGNATURES = {
                                   _vp, _i64, _i32, _vp, _i64, _vp]),
     "attention_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _pi64]),
     "attention_split_fp32": (_i32, [_i64, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i64, _vp]),
+    "attention_split_fp32_static": (_i32, [_i64, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp]),
 }
 EXPORTS = tuple(_SIGNATURES)
 
@@ -345,6 +346,16 @@ def attention_workspace_bytes(nq, nk, d, algo=1) -> int:
     b = C.c_int64()
     _check(load().attention_workspace_bytes(nq, nk, d, algo, C.byref(b)), "attention_workspace_bytes")
     return b.value
+
+
+ATTN_STATIC_SCRATCH_BYTES = 64 << 20   # MFL_ATTN_STATIC_SCRATCH_BYTES
+
+
+def attention_split_fp32_static(nq, nk, d, q, k, v, chains, algo, o, stream=None) -> None:
+    _need("attention_split_fp32_static", q=(q, _extent(nq, d, d, 4)), k=(k, _extent(nk, d, d, 4)),
+          v=(v, _extent(nk, d, d, 4)), o=(o, _extent(nq, d, d, 4)))
+    _check(load().attention_split_fp32_static(nq, nk, d, _ptr(q), _ptr(k), _ptr(v), chains, algo, _ptr(o),
+                                              _stream(stream)), "attention_split_fp32_static")
 
 
 def attention_split_fp32(nq, nk, d, q, k, v, chains, algo, o, workspace, workspace_bytes, stream=None) -> None:

@@ -14,6 +14,8 @@
 // fp16's subnormal range and lose most of their lo half.  softmax(S) V equals
 // (P~ V) / l exactly in real arithmetic.  This version materialises S / P~ in
 // the caller's workspace (HBM-bound); it keeps every step on the device.
+#include <mutex>
+
 #include "attention_fused.hpp"
 #include "gemm_split.hpp"
 
@@ -182,31 +184,30 @@ bool fused_fits(int64_t nk) { return nk * kAttnD * 2 <= (int64_t)UINT32_MAX; }
 
 using namespace mfl;
 
-extern "C" int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int algo, int64_t* bytes) {
-  if (!bytes || algo < 0 || algo > 2) return MFL_EINVAL;
-  if (!valid_sizes(nq, nk, d) || (algo >= 1 && !fused_fits(nk))) return MFL_EUNSUPPORTED;
-  *bytes = algo == 0 ? plan(nq, nk, d).total : attn_fused_workspace(nq, nk, algo == 2);
-  return MFL_OK;
-}
+namespace {
 
-extern "C" int attention_split_fp32(int64_t nq, int64_t nk, int64_t d, const float* q, const float* k, const float* v,
-                                    int chains, int algo, float* o, void* workspace, int64_t workspace_bytes,
-                                    void* stream) {
+// Checks of everything but the workspace (host only, before any HIP call).
+int attention_args(int64_t nq, int64_t nk, int64_t d, const float* q, const float* k, const float* v, int chains,
+                   int algo, const float* o) {
   if (chains != 1 && chains != 2) return MFL_EINVAL;
   if (algo < 0 || algo > 2) return MFL_EINVAL;
   if (!valid_sizes(nq, nk, d)) return nq < 0 || nk < 0 || d < 0 ? MFL_EINVAL : MFL_EUNSUPPORTED;
-  if (!q || !k || !v || !o || !workspace) return MFL_EINVAL;
+  if (!q || !k || !v || !o) return MFL_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return MFL_EINVAL;
-  if (((uintptr_t)workspace & 255) != 0) return MFL_EINVAL;
-  hipStream_t s = (hipStream_t)stream;
-  if (algo >= 1) {
-    if (!fused_fits(nk)) return MFL_EUNSUPPORTED;
-    const bool skv = algo == 2;
-    if (workspace_bytes < attn_fused_workspace(nq, nk, skv)) return MFL_EINVAL;
-    return launch_attn_fused(nq, nk, q, k, v, chains, skv, o, workspace, s);
-  }
+  if (algo >= 1 && !fused_fits(nk)) return MFL_EUNSUPPORTED;
+  return MFL_OK;
+}
+
+int64_t attention_need(int64_t nq, int64_t nk, int64_t d, int algo) {
+  return algo == 0 ? plan(nq, nk, d).total : attn_fused_workspace(nq, nk, algo == 2);
+}
+
+// Launches the algorithm on a workspace of at least attention_need bytes
+// (arguments already checked).
+int attention_launch(int64_t nq, int64_t nk, int64_t d, const float* q, const float* k, const float* v, int chains,
+                     int algo, float* o, void* workspace, hipStream_t s) {
+  if (algo >= 1) return launch_attn_fused(nq, nk, q, k, v, chains, algo == 2, o, workspace, s);
   const Workspace w = plan(nq, nk, d);
-  if (workspace_bytes < w.total) return MFL_EINVAL;
   char* ws = (char*)workspace;
   float* S = (float*)(ws + w.s_off);
   float* m = (float*)(ws + w.m_off);
@@ -234,4 +235,63 @@ extern "C" int attention_split_fp32(int64_t nq, int64_t nk, int64_t d, const flo
   hipLaunchKernelGGL(reduce_slices, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, w.splits, nq * d, l,
                      o, D, total);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int algo, int64_t* bytes) {
+  if (!bytes || algo < 0 || algo > 2) return MFL_EINVAL;
+  if (!valid_sizes(nq, nk, d) || (algo >= 1 && !fused_fits(nk))) return MFL_EUNSUPPORTED;
+  *bytes = attention_need(nq, nk, d, algo);
+  return MFL_OK;
+}
+
+extern "C" int attention_split_fp32(int64_t nq, int64_t nk, int64_t d, const float* q, const float* k, const float* v,
+                                    int chains, int algo, float* o, void* workspace, int64_t workspace_bytes,
+                                    void* stream) {
+  int st = attention_args(nq, nk, d, q, k, v, chains, algo, o);
+  if (st != MFL_OK) return st;
+  if (!workspace || ((uintptr_t)workspace & 255) != 0) return MFL_EINVAL;
+  if (workspace_bytes < attention_need(nq, nk, d, algo)) return MFL_EINVAL;
+  return attention_launch(nq, nk, d, q, k, v, chains, algo, o, workspace, (hipStream_t)stream);
+}
+
+// ---- allocation-free variant -------------------------------------------------
+// The workspace lives in a file-scope device array, one copy per GPU.  Its
+// name is a host-side stand-in in host code: the device address of this GPU's
+// copy comes from hipGetSymbolAddress, taken once per device on the first call
+// made with that device current, and only that address is handed to kernels.
+namespace {
+
+static __device__ __attribute__((aligned(256))) char scratch[MFL_ATTN_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MFL_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return MFL_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MFL_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MFL_OK;
+}
+
+}  // namespace
+
+extern "C" int attention_split_fp32_static(int64_t nq, int64_t nk, int64_t d, const float* q, const float* k,
+                                           const float* v, int chains, int algo, float* o, void* stream) {
+  const int st = attention_args(nq, nk, d, q, k, v, chains, algo, o);
+  if (st != MFL_OK) return st;
+  if (attention_need(nq, nk, d, algo) > MFL_ATTN_STATIC_SCRATCH_BYTES) return MFL_ESCRATCH;
+  void* ws = nullptr;
+  const int sp = device_scratch(&ws);
+  if (sp != MFL_OK) return sp;
+  return attention_launch(nq, nk, d, q, k, v, chains, algo, o, ws, (hipStream_t)stream);
 }

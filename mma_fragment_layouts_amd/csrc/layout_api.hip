@@ -85,6 +85,7 @@ extern "C" const char* mfl_status_string(int status) {
     case MFL_EOVERFLOW: return "MFL_EOVERFLOW: result does not fit";
     case MFL_EUNSUPPORTED: return "MFL_EUNSUPPORTED: not implemented for these arguments";
     case MFL_EHIP: return "MFL_EHIP: HIP launch failed";
+    case MFL_ESCRATCH: return "MFL_ESCRATCH: needs more than the static scratch array holds";
     default: return "unknown mfl status";
   }
 }

@@ -39,7 +39,7 @@ def test_library_resolves_every_symbol():
 def test_version_and_status_strings(lib):
     assert lib.mfl_version() >= 100
     assert lib.status_string(0) == "MFL_OK"
-    for st in (-1, -2, -3, -4):
+    for st in (-1, -2, -3, -4, -5):
         assert lib.status_string(st).startswith("MFL_E")
     assert "unknown" in lib.status_string(17)
 
