@@ -227,6 +227,66 @@ __device__ __forceinline__ void mma_slab(const uint16_t* sA, const uint16_t* sB,
   }
 }
 
+// mma_slab with part of the slab's last MFMA K step carried over the next
+// barrier: the MFMAs of the last CARRY fragment rows of the last K step are not
+// issued here; their A fragments (ca) and the step's B fragments (cb) stay in
+// registers, and the next call issues them (`pending`) right after its first
+// fragment reads, so every wave has MFMAs ready while the reads that follow the
+// barrier are in flight.  Each accumulator still receives its MFMAs in the same
+// K order, so the result is bit-identical to mma_slab.  After the last slab the
+// caller issues the carried MFMAs with mma_carried.
+template <int SHAPE, int DT, int TM, int TN, int CARRY>
+__device__ __forceinline__ void mma_carried(const u32x4 (&ca)[CARRY], const u32x4 (&cb)[TN],
+                                            typename Shape<SHAPE>::Acc (&acc)[TM][TN]) {
+#pragma unroll
+  for (int c = 0; c < CARRY; ++c)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[TM - CARRY + c][j] = mfma<SHAPE, DT>(ca[c], cb[j], acc[TM - CARRY + c][j]);
+}
+
+template <int SHAPE, int DT, int TM, int TN, int BK, int CARRY, bool MASKK = false, class RA, class RB>
+__device__ __forceinline__ void mma_slab_carry(const uint16_t* sA, const uint16_t* sB, const RA& fa, const RB& fb,
+                                               typename Shape<SHAPE>::Acc (&acc)[TM][TN], u32x4 (&ca)[CARRY],
+                                               u32x4 (&cb)[TN], bool pending, int kvalid = BK) {
+  constexpr int MN = Shape<SHAPE>::MN, KM = Shape<SHAPE>::K, KS = BK / KM;
+  static_assert(CARRY > 0 && CARRY < TM, "carry some but not all fragment rows");
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    u32x4 a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = frag_read(sA, fa, kk, i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = frag_read(sB, fb, kk, j);
+    if constexpr (MASKK) {
+      if (kvalid < BK && kk * KM + 8 * ((int)(threadIdx.x & 63) / MN) >= kvalid) {  // kvalid is wave-uniform
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[j] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (kk == 0 && pending) {
+      // the empty asm statements are ordered after the barrier that precedes
+      // this call, and the carried MFMAs depend on them
+#pragma unroll
+      for (int c = 0; c < CARRY; ++c) asm volatile("" : "+v"(ca[c]));
+      mma_carried<SHAPE, DT, TM, TN, CARRY>(ca, cb, acc);
+    }
+    constexpr int last = KS - 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      if (kk != last || i < TM - CARRY)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma<SHAPE, DT>(a[i], b[j], acc[i][j]);
+    if (kk == last) {
+#pragma unroll
+      for (int c = 0; c < CARRY; ++c) ca[c] = a[TM - CARRY + c];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) cb[j] = b[j];
+    }
+  }
+}
+
 // Wait until at most N of this wave's vector-memory operations (the
 // direct-to-LDS loads included) are outstanding.
 template <int N>
