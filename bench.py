@@ -79,8 +79,8 @@ def best_of(fn, stream, warm=3, rounds=3, per=20, settle_ms=30.0):
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_4096_bf16_traffic.json")
 # The headline kernel: mangled name in the code object, and as the profiler names it.
-HEADLINE_SYMBOL = "gemm_fast_kernelILi256ELi256ELi4ELi4ELi0ELi1ELi2ELb0ELb0ELb0E"
-HEADLINE_PROFILED = "gemm_fast_kernel<256, 256, 4, 4, 0, 1, 2, false, false, false>"
+HEADLINE_SYMBOL = "gemm_fast_kernelILi256ELi256ELi4ELi4ELi0ELi1ELi2ELb0ELb0ELb0ELi2E"
+HEADLINE_PROFILED = "gemm_fast_kernel<256, 256, 4, 4, 0, 1, 2, false, false, false, 2>"
 
 
 def headline_digest():
@@ -345,11 +345,14 @@ def gemm_orders(torch, mfl, inputs, stream, dev, q16, out):
     for oa in (mfl.ROW_MAJOR, mfl.COL_MAJOR):
         for ob in (mfl.COL_MAJOR, mfl.ROW_MAJOR):
             da, db = q16(store_a[oa], mfl.BF16), q16(store_b[ob], mfl.BF16)
-            ms = best_of(lambda: mfl.gemm_tile_mma(mfl.BF16, n, n, n, da, 4160, oa, db, 4160, ob, c, n, 0, stream),
-                         stream)
-            tf = 2 * n ** 3 / ms / 1e9
-            res[f"A_{name[oa]}_B_{name[ob]}"] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1),
-                                                 "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            # both instructions: a k-major operand moves the same LDS bytes per
+            # flop with either, but the reads differ in count and phase pattern
+            for shape, suffix in ((0, ""), (1, "_32x32x16")):
+                ms = best_of(lambda: mfl.gemm_tile_mma_shape(shape, mfl.BF16, n, n, n, da, 4160, oa, db, 4160, ob, c, n,
+                                                             0, stream), stream)
+                tf = 2 * n ** 3 / ms / 1e9
+                res[f"A_{name[oa]}_B_{name[ob]}{suffix}"] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                                                             "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
             del da, db
     out["gemm_4096_bf16_orders"] = res
     # The K-contiguous order with fp16 operands, and with the 32x32x16 instruction.
