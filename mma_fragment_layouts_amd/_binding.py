@@ -15,7 +15,10 @@ import ctypes as C
 import os
 from typing import Optional, Tuple
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmfl.so")
+# MFL_LIBRARY overrides the library file (the host-sanitizer test loads an
+# instrumented build through it); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("MFL_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
+                                                         "libmfl.so")
 
 # enums (values fixed by include/mfl.h)
 OK, EINVAL, EOVERFLOW, EUNSUPPORTED, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5

@@ -3,6 +3,13 @@
 Every ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in
 parallel) and the objects are linked into ``lib/libmfl.so`` next to this file.
 Run ``python -m mma_fragment_layouts_amd.build`` or call ``build()``.
+
+``build(sanitize=True)`` (``--sanitize``) makes a second library,
+``_build_san/libmfl_san.so``, whose host code is instrumented with
+AddressSanitizer and UndefinedBehaviorSanitizer (the device code is built as
+usual): the argument validation, workspace arithmetic and dispatch of the C ABI
+run under the sanitizers on a CPU-only machine.  It needs the ASan runtime
+preloaded (see ``sanitizer_runtime()``).
 """
 from __future__ import annotations
 
@@ -26,13 +33,28 @@ FLAGS = [
 ]
 
 
+OBJ_SAN = os.path.join(HERE, "_build_san")
+LIB_SAN = os.path.join(OBJ_SAN, "libmfl_san.so")
+# host code only: each -fsanitize= goes right after -Xarch_host
+SAN_FLAGS = ["-O1", "-g", "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fsanitize=address",
+             "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that an uninstrumented
+    program (python) must preload to load libmfl_san.so."""
+    out = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return out.stdout.strip()
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, sanitize: bool = False) -> str:
+    obj = os.path.join(OBJ_SAN if sanitize else OBJ, os.path.basename(src)[:-4] + ".o")
+    flags = [f for f in FLAGS if f != "-O3"] + SAN_FLAGS if sanitize else FLAGS
+    cmd = [HIPCC, *flags, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -42,23 +64,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = True) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    os.makedirs(os.path.dirname(LIB), exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = True, sanitize: bool = False) -> str:
+    out = LIB_SAN if sanitize else LIB
+    os.makedirs(OBJ_SAN if sanitize else OBJ, exist_ok=True)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
+        objs = list(ex.map(lambda src: _compile(src, sanitize), srcs))
+    tmp = out + ".tmp"
+    link_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"] if sanitize else []
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_san, *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {out} from {len(srcs)} sources")
+    return out
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--sanitize" in sys.argv)
