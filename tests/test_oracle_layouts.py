@@ -8,6 +8,7 @@ The two CDNA4 maps are checked as bijections here; their device agreement is
 the GPU probe test's job."""
 import os
 
+import numpy as np
 import pytest
 
 from oracle import layouts as L
@@ -201,6 +202,38 @@ def test_operand_enumerator_catches_mutants():
     swapped = mut(lambda l, i: (4 * (l % 4) + l // 16, 8 * ((l // 4) % 4) + i))                # lane digits swapped
     assert L.operand_is_bijection(swapped)
     assert any(swapped.coords(l, 0) != om.coords(l, 0) for l in range(64))
+
+
+@pytest.mark.parametrize("key", sorted(L.OPERAND_MAPS))
+def test_operand_matrix_offset_places_the_tile_block(key):
+    """Scatter every (lane, i) of one operand fragment through
+    operand_matrix_offset into flat storage and read it back with numpy's own
+    row-major indexing: the fragment fills exactly the rows x cols block at the
+    origin, each element once, and the column-major placement is the transpose
+    of the same storage (numpy's .T), holding the same block."""
+    om = L.OPERAND_MAPS[key]
+    row0, col0, ld = 5, 3, om.cols + om.rows + 11
+    rows_total = row0 + om.rows + 2
+    cols_total = col0 + om.cols + 2
+    ids = {}
+    flat_r = np.full(rows_total * ld, -1, dtype=np.int64)        # row-major: (rows_total, ld)
+    flat_c = np.full(cols_total * ld, -1, dtype=np.int64)        # column-major: (cols_total, ld)
+    for lane in range(om.lanes):
+        for i in range(om.per_lane):
+            ident = lane * om.per_lane + i
+            ids[ident] = True
+            o_r = L.operand_matrix_offset(om, lane, i, row0, col0, ld, 0)
+            o_c = L.operand_matrix_offset(om, lane, i, row0, col0, ld, 1)
+            assert flat_r[o_r] == -1 and flat_c[o_c] == -1
+            flat_r[o_r] = ident
+            flat_c[o_c] = ident
+    mat_r = flat_r.reshape(rows_total, ld)
+    mat_c = flat_c.reshape(cols_total, ld).T                      # (ld, cols_total), row index first
+    block = (slice(row0, row0 + om.rows), slice(col0, col0 + om.cols))
+    assert sorted(mat_r[block].ravel().tolist()) == sorted(ids)
+    assert (mat_r >= 0).sum() == om.rows * om.cols               # nothing outside the block
+    assert np.array_equal(mat_c[block], mat_r[block])
+    assert (mat_c >= 0).sum() == om.rows * om.cols
 
 
 def test_operand_matrix_offset_orders_and_overflow():
