@@ -183,8 +183,9 @@ static int launch_fast(const void* a, int64_t lda, const void* b, int64_t ldb, f
   // Whole 256 x 256 tiles (16 waves) with the 16x16x32 instruction carry two of
   // a wave's four fragment rows of each slab's last MFMA K step over the next
   // barrier (measured +1.4 % at 4096^3; the EDGE variant has no registers left
-  // for the carried fragments and does not carry).
-  constexpr int CARRY = (BM == 256 && BN == 256 && SHAPE == 0) ? 2 : 0;
+  // for the carried fragments and does not carry); whole 192 x 192 tiles carry
+  // one row.
+  constexpr int CARRY = SHAPE != 0 ? 0 : (BM == 256 && BN == 256) ? 2 : (BM == 192 && BN == 192) ? 1 : 0;
   if (M % BM == 0 && N % BN == 0 && K % 64 == 0)
     hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WGM, WGN, SHAPE, DT, STAGES, AKM, BKM, false, CARRY>), grid, block, 0,
                        stream, A, B, c, (uint32_t)lda, (uint32_t)ldb, (uint32_t)ldc, M, N, K, tiles_m, tiles_n,
@@ -239,7 +240,8 @@ template <int DT, bool AKM, bool BKM>
 static int dispatch_fast(int shape, const void* a, int64_t lda, const void* b, int64_t ldb, float* c, int64_t ldc,
                          int M, int N, int K, int accumulate, hipStream_t s) {
   // The largest tile that still gives the chip at least 128 workgroups:
-  // 256 x 256 (16 waves of 64 x 64), 128 x 128 (4 waves of 64 x 64), or for
+  // 256 x 256 (16 waves of 64 x 64; 192 x 192 when that fills one round
+  // better, below), 128 x 128 (4 waves of 64 x 64), or for
   // small problems with K-contiguous operands 64 x 64 (2 waves of 32 x 64),
   // where a single big tile would leave all but a few CUs idle.  Sizes that
   // are not tile multiples run the EDGE variant of the same kernel.
@@ -256,6 +258,15 @@ static int dispatch_fast(int shape, const void* a, int64_t lda, const void* b, i
     return s32 ? launch_fast<128, 128, 2, 2, 1, DT, AKM, BKM>(a2, lda, b, ldb, c2, ldc, M - M1, N, K, accumulate, s)
                : launch_fast<128, 128, 2, 2, 0, DT, AKM, BKM>(a2, lda, b, ldb, c2, ldc, M - M1, N, K, accumulate, s);
   }
+  // One partial round of 256 x 256 tiles (128-255 of them, e.g. 3072^3: 144)
+  // leaves CUs idle; when 192 x 192 tiles (12 waves of 64 x 48, three per SIMD)
+  // cover C in one round they run on more CUs: 3072^3 50 us against 60 us
+  // (256 workgroups against 144).  The 192-wide slab is K-contiguous only, and
+  // a 48-wide wave tile needs the 16x16x32 instruction.  Above one round the
+  // extra rounds cost more than the fill gains (3328^3: 96 us against 67 us).
+  if constexpr (!AKM && !BKM)
+    if (!s32 && count(256) >= 128 && count(256) < 256 && count(192) <= 256)
+      return launch_fast<192, 192, 3, 4, 0, DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
   if (count(256) >= 128)
     return s32 ? launch_fast<256, 256, 4, 4, 1, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)
                : launch_fast<256, 256, 4, 4, 0, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);

@@ -1,7 +1,8 @@
 """gemm_tile_mma against the oracle: fp64 product of the quantised inputs,
 normwise relative error <= 1e-5; bit-exact on integer-valued inputs; all four
-operand orders; ragged edges; NaN padding never read; the 4096^3 bf16 case in
-the launch configuration the benchmark times (every element of C)."""
+operand orders; every tile configuration of the fast path (64, 128, 192 and
+256 wide); ragged edges; NaN padding never read; the 4096^3 bf16 case in the
+launch configuration the benchmark times (every element of C)."""
 import numpy as np
 import pytest
 import torch
@@ -185,7 +186,9 @@ def test_dense_4096_full(shape, fmt):
                                              ((192, 320, 128), 1),     # 64 x 64 (not a multiple of 128)
                                              ((1024, 1024, 512), 0),   # 64 x 64, 256 workgroups
                                              ((2048, 2048, 256), 1),   # 128 x 128, 256 workgroups
-                                             ((2048, 4096, 128), 0)])  # 256 x 256, 128 workgroups
+                                             ((2048, 4096, 128), 0),   # 256 x 256, 128 workgroups
+                                             ((3072, 3072, 3072), 0),  # 192 x 192 (16x16x32), 256 workgroups
+                                             ((3072, 3072, 512), 1)])
 def test_fast_path_tile_sizes(mnk, accumulate, shape, fmt):
     m, n, k = mnk
     rng = np.random.default_rng(m + n + k + shape)
@@ -211,6 +214,7 @@ ORDERS = [(mfl.ROW_MAJOR, mfl.COL_MAJOR), (mfl.ROW_MAJOR, mfl.ROW_MAJOR), (mfl.C
 @pytest.mark.parametrize("shape", [0, 1])
 @pytest.mark.parametrize("mnk,accumulate", [((4096, 4096, 128), 0),   # 256 x 256 tiles
                                             ((2048, 1024, 192), 0),   # 128 x 128 tiles
+                                            ((3072, 3072, 256), 1),   # 192 x 192 (K-contiguous, 16x16x32), 256 x 256
                                             ((256, 384, 320), 1),     # 128 x 128 (k-major), 64 x 64 (K-contiguous)
                                             ((128, 128, 64), 0)])     # one tile, one K step
 def test_fast_path_all_orders_bit_identical(mnk, accumulate, shape, fmt):
@@ -272,7 +276,9 @@ def test_dense_4096_bf16_other_orders(orders, shape):
                                             ((2056, 1160, 128), 1),
                                             ((1000, 520, 200), 0),     # K not a multiple of 64: masked last slab
                                             ((264, 136, 8), 1),        # a single partial K slab
-                                            ((4000, 4096, 4040), 0)])  # 256 x 256 tiles, every edge ragged
+                                            ((4000, 4096, 4040), 0),   # 256 x 256 tiles, every edge ragged
+                                            ((2904, 3000, 1000), 1),   # 192 x 192 (K-contiguous), 256 x 256
+                                            ((3072, 2824, 200), 0)])   # 192 x 192 with ragged N and K
 def test_fast_path_ragged_all_orders(mnk, accumulate, fmt):
     m, n, k = mnk
     rng = np.random.default_rng(m + 7 * n + k)
