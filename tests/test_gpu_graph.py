@@ -141,3 +141,28 @@ def test_graph_attention(algo):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o_graph, o_eager), f"replay {r}"
+
+
+@pytest.mark.parametrize("algo", [mfl.ATTN_MATERIALISED, mfl.ATTN_FUSED, mfl.ATTN_FUSED_SPLIT_KV])
+def test_graph_attention_static(algo):
+    """attention_split_fp32_static, the entry point for callers that cannot
+    allocate: its workspace is the library's static device array, so the
+    captured graph holds only kernel launches on that array."""
+    nq, nk, d = 256, 4096, 128
+    q, k, v = (dev32(x) for x in inputs.attention(nq, nk))
+    say("graph attention static", algo)
+
+    def call(o, st):
+        mfl.attention_split_fp32_static(nq, nk, d, q, k, v, 2, algo, o, st)
+
+    o_eager = torch.full((nq, d), np.nan, device=device())
+    call(o_eager, stream())
+    torch.cuda.synchronize()
+    o_graph = torch.empty((nq, d), device=device())
+    g = capture(lambda st: call(o_graph, st))
+    for r in range(REPLAYS):
+        o_graph.fill_(np.nan)
+        eager_noise((64, 64))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_graph, o_eager), f"replay {r}"
