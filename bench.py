@@ -272,7 +272,7 @@ def mfma_ceiling(torch, mfl, stream, iters=512):
 
 EXTRA = ("gemm_256", "gemm_orders", "block_repeat", "split", "attention")
 # opt-in legs (not run by default)
-EXTRA_OPTIONAL = ("gemm_sizes",)
+EXTRA_OPTIONAL = ("gemm_sizes", "attention_fused")
 
 
 def extra_workloads(torch, mfl, inputs, stream, which=EXTRA):
@@ -297,6 +297,8 @@ def extra_workloads(torch, mfl, inputs, stream, which=EXTRA):
         attention(torch, mfl, inputs, stream, dev, out)
     if "gemm_sizes" in which:
         gemm_sizes(torch, mfl, inputs, stream, dev, q16, out)
+    if "attention_fused" in which:
+        attention_fused(torch, mfl, inputs, stream, dev, out)
     return out
 
 
@@ -474,6 +476,23 @@ def attention(torch, mfl, inputs, stream, dev, out):
             del ws
         out[key] = att
         del dq, dk, dv, o
+
+
+def attention_fused(torch, mfl, inputs, stream, dev, out):
+    """The fused algorithm alone at 2048 x 32768 x 128 with 2 chains: the only
+    attention launches of the run, so that a counter or trace run of this leg
+    sees that kernel at that size and nothing else of its kind."""
+    q, k, v = inputs.attention(2048, 32768)
+    dq, dk, dv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    o = torch.empty((2048, 128), device=dev)
+    wsb = mfl.attention_workspace_bytes(2048, 32768, 128, mfl.ATTN_FUSED)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ms = best_of(lambda: mfl.attention_split_fp32(2048, 32768, 128, dq, dk, dv, 2, mfl.ATTN_FUSED, o, ws, wsb, stream),
+                 stream, rounds=2, per=5)
+    mf = 2 * 2 * 2 * 2048 * 32768 * 128 / ms / 1e9
+    out["attention_2048x32768_fused"] = {"ms": round(ms, 4), "mfma_tflops": round(mf, 1),
+                                         "frac_mfma_peak": round(mf / PEAK_BF16_TFLOPS, 4)}
+    del dq, dk, dv, o, ws
 
 
 def main():

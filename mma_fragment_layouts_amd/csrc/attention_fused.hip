@@ -18,6 +18,21 @@ __device__ __forceinline__ Split2 split2(float a, float b) {
   return {__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};
 }
 
+// The same split with x - hi taken by v_fma_mix_f32 straight from the fp16 hi
+// (x * 1 - hi in one instruction; the difference is exact, so the result is the
+// same as converting hi back and subtracting: checked on the device for every
+// fp32 value in [2^-40, 2^9), fp16-subnormal hi included).  Two vector
+// instructions fewer per pair.
+__device__ __forceinline__ Split2 split2_mix(float a, float b) {
+  const h16x2 h = __builtin_convertvector(f32x2{a, b}, h16x2);
+  const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+  float r0, r1;
+  asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(r0) : "v"(a), "v"(hb));
+  asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "=v"(r1) : "v"(b), "v"(hb));
+  const h16x2 l = __builtin_convertvector(f32x2{r0, r1}, h16x2);
+  return {hb, __builtin_bit_cast(uint32_t, l)};
+}
+
 // Elementwise preparation of K and V (both nk x 128 fp32, key-major) into
 // K16 and V16 (fp16, round to nearest even, same layout); with SKV also the lo
 // planes Kl and Vl, lo = RNE16(x - hi).  Thread t of workgroup b converts the
@@ -192,13 +207,18 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
   const FragOffsets<0, BK> fo(0, lane);  // K16 reads: lane row lr, chunk 4*kk + g
   const KmFrag<0, kAttnD, kAttnD, 8> fv(0, lane);  // V16 reads: 8 dim tiles, transpose reads
 
+  float mref = -INFINITY, lsum = 0.f;  // per-query reference and row sum of P~
+
   // GEMM1 of one chunk: S^T (64 keys x 16 queries) = K16 . (log2e Q)^T, hi and
-  // lo products in chains sh / sl (CHAINS == 2) or both in sh.
+  // lo products in chains sh / sl (CHAINS == 2) or both in sh.  The hi chain
+  // starts from -mref (0 on the first chunk, which has no reference yet), so
+  // the chunk's scores come out relative to the reference.
   auto gemm1 = [&](int chunk, f32x4 (&sh)[4], f32x4 (&sl)[4]) {
     const uint16_t* st = lds + (chunk % STAGES) * STAGE;
+    const float mb = chunk > 0 ? -mref : 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      sh[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sh[kt] = f32x4{mb, mb, mb, mb};
       sl[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
@@ -225,13 +245,13 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
     oh[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     ol[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float mref = -INFINITY, lsum = 0.f;
 
   // Online softmax, in two parts.  Lanes lr, lr+16, lr+32, lr+48 share a query.
-  // (1) Chains added, chunk max, and the move of the reference when the max
-  // passes it by more than the slack (wave-uniform branch, rare after the
-  // first chunk).
-  auto update_ref = [&](f32x4 (&sh)[4], const f32x4 (&sl)[4]) {
+  // (1) Chains added (giving t = s - mref, or s on the first chunk), chunk
+  // max, and the move of the reference when the max passes it by more than
+  // the slack (wave-uniform branch, taken on the first chunk and rarely
+  // after): mref rises by the overshoot, t falls by it, O and l are rescaled.
+  auto update_ref = [&](int chunk, f32x4 (&sh)[4], const f32x4 (&sl)[4]) {
     float cmax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -240,8 +260,9 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
       for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, sh[kt][j]);
     }
     cmax = max_over_lane_groups(cmax);
-    if (__builtin_amdgcn_ballot_w64(cmax > mref + kAttnSlack) != 0) {
-      const float mnew = fmaxf(mref, cmax);
+    if (chunk == 0 || __builtin_amdgcn_ballot_w64(cmax > kAttnSlack) != 0) {
+      const float shift = chunk == 0 ? cmax : fmaxf(cmax, 0.f);
+      const float mnew = (chunk == 0 ? 0.f : mref) + shift;
       const float sc = __builtin_amdgcn_exp2f(mref - mnew);  // 0 on the first chunk (mref = -inf)
       mref = mnew;
       lsum *= sc;
@@ -250,10 +271,12 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
         oh[i] = oh[i] * sc;
         if constexpr (CHAINS == 2) ol[i] = ol[i] * sc;
       }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) sh[kt] = sh[kt] - shift;
     }
   };
-  // (2) P~ = 2^(s - mref), its row-sum contribution, and the split P~^T
-  // fragments of GEMM2.
+  // (2) P~ = 2^t, its row-sum contribution, and the split P~^T fragments of
+  // GEMM2.
   auto exp_split = [&](const f32x4 (&s)[4], u32x4 (&ph)[2], u32x4 (&pl)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -261,11 +284,11 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
       for (int e = 0; e < 4; ++e) {
         // K positions 2e, 2e+1 of block t: keys of tile 2t (e < 2) or 2t+1
         const f32x4& x = s[2 * t + (e >> 1)];
-        const float p0 = __builtin_amdgcn_exp2f(x[2 * (e & 1)] - mref);
-        const float p1 = __builtin_amdgcn_exp2f(x[2 * (e & 1) + 1] - mref);
+        const float p0 = __builtin_amdgcn_exp2f(x[2 * (e & 1)]);
+        const float p1 = __builtin_amdgcn_exp2f(x[2 * (e & 1) + 1]);
         lsum += p0;
         lsum += p1;
-        const Split2 sp2 = split2(p0, p1);
+        const Split2 sp2 = split2_mix(p0, p1);
         ph[t][e] = sp2.hi;
         pl[t][e] = sp2.lo;
       }
@@ -303,7 +326,7 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(const float* __restrict
     f32x4 sh[4], sl[4];
     gemm1(c, sh, sl);
     u32x4 ph[2], pl[2];
-    update_ref(sh, sl);
+    update_ref(c, sh, sl);
     exp_split(sh, ph, pl);
     gemm2(c, ph, pl);
   }
