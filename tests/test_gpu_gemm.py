@@ -376,3 +376,43 @@ def test_wave_quantisation_split_k_major(oa, ob, m, n, k):
         assert torch.equal(part, c[r0:r0 + 256]), r0
     rows = np.random.default_rng(22).choice(m, 16, replace=False)
     assert R.rel_error(host(c)[rows], R.gemm_ref(a[rows], bt, "bf16")) <= TOL
+
+
+# Leading dimensions at the fast path's 32-bit buffer-offset limit.  The fast
+# path addresses an operand through a 32-bit buffer extent (a K-contiguous
+# operand: one panel of at most 256 rows; a k-major one: all K rows) and C
+# through 256 rows of ldc; just below those limits it still runs, at or past
+# them the dispatcher takes the generic path, whose addresses are 64-bit.  The
+# storage here is 4-4.3 GiB per operand; only the M x K (K x N) block is set.
+@pytest.mark.parametrize("side", ["below", "past"])
+@pytest.mark.parametrize("oa,ob", [(mfl.ROW_MAJOR, mfl.COL_MAJOR), (mfl.COL_MAJOR, mfl.ROW_MAJOR)])
+def test_leading_dimensions_at_the_32_bit_limit(side, oa, ob):
+    m = n = k = 256
+    ld = (1 << 23) - 64 if side == "below" else (1 << 23) + 64   # 256 * ld * 2 bytes vs 2^32
+    ldc = (1 << 22) - 64 if side == "below" else (1 << 22) + 64  # 256 * ldc * 4 bytes vs 2^32
+    rng = np.random.default_rng(41 + (side == "past"))
+    a = rng.uniform(-1, 1, (m, k)).astype(np.float32)
+    b = rng.uniform(-1, 1, (k, n)).astype(np.float32)
+    ref = R.gemm_ref(a, np.ascontiguousarray(b.T), "bf16")
+
+    def big(x_logical, order):
+        """Device storage rows x ld (bf16, zeros) holding the logical matrix in `order`."""
+        block = x_logical if order == mfl.ROW_MAJOR else np.ascontiguousarray(x_logical.T)
+        s = torch.zeros((block.shape[0], ld), dtype=torch.int16, device=device())
+        s[:, : block.shape[1]] = q16(block, "bf16")
+        return s
+
+    say("gemm ld at 32-bit limit", side, oa, ob, ld, ldc)
+    sa, sb = big(a, oa), big(b, ob)
+    c = torch.full((m, ldc), SENTINEL, device=device())
+    c[:, :n] = np.nan
+    mfl.gemm_tile_mma(mfl.BF16, m, n, k, sa, ld, oa, sb, ld, ob, c, ldc, 0, stream())
+    out = host(c[:, :n])
+    assert not np.isnan(out).any()
+    assert R.rel_error(out, ref) <= TOL
+    assert bool((c[:, n:] == SENTINEL).all()), "padding of C was written"
+    # the same values through compact storage give the same bits
+    small = run_gemm("bf16", a, b, oa, ob)
+    assert np.array_equal(out.view(np.uint32), small.view(np.uint32))
+    del sa, sb, c
+    torch.cuda.empty_cache()
