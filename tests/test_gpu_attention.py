@@ -137,3 +137,34 @@ def test_attention_split_kv_full_size_removes_the_rounding_floor():
     assert errs[(mfl.ATTN_FUSED_SPLIT_KV, 2)] <= 5e-6
     assert errs[(mfl.ATTN_FUSED_SPLIT_KV, 1)] <= 5e-6
     assert errs[(mfl.ATTN_FUSED, 2)] >= 10 * errs[(mfl.ATTN_FUSED_SPLIT_KV, 2)]
+
+
+# The largest key count the fused kernels take (nk * 128 * 2 bytes of K16 within
+# a 32-bit buffer extent): 2^24 - 128 keys, one block of 128 queries.  With
+# K = 0 every score is 0, P~ = 1 and O is the mean of the V rows; V's rows are
+# 1 + j/8 (j = bits 16-18 of the key index), exact in fp16, so every partial
+# sum of the kernels is an integer below 2^24 and the result is the exact mean
+# up to the last fp32 roundings.  A key counted twice, skipped, or read from
+# the wrong place past 2^23 keys changes the mean.
+@pytest.mark.parametrize("algo", [mfl.ATTN_MATERIALISED, mfl.ATTN_FUSED, mfl.ATTN_FUSED_SPLIT_KV])
+def test_attention_maximum_keys(algo):
+    nq, nk, d = 128, (1 << 24) - 128, 128
+    say("attention maximum keys", algo, nk)
+    kidx = torch.arange(nk, device=device())
+    vcol = 1.0 + ((kidx >> 16) & 7).to(torch.float32) / 8.0
+    v = vcol[:, None].expand(nk, d).contiguous()
+    del kidx, vcol
+    k = torch.zeros((nk, d), device=device())
+    q = torch.from_numpy(np.random.default_rng(5).standard_normal((nq, d)).astype(np.float32)).to(device())
+    wsb = mfl.attention_workspace_bytes(nq, nk, d, algo)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=device())
+    o = torch.full((nq, d), np.nan, device=device())
+    mfl.attention_split_fp32(nq, nk, d, q, k, v, 2, algo, o, ws, wsb, stream())
+    out = host(o)
+    del ws, k, v
+    torch.cuda.empty_cache()
+    full, rest = divmod(nk, 1 << 16)
+    total = sum((8 + (b & 7)) * (1 << 16) for b in range(full)) + (8 + (full & 7)) * rest   # in eighths
+    want = total / 8.0 / nk
+    assert not np.isnan(out).any()
+    assert np.max(np.abs(out - want)) <= 1e-6 * want
