@@ -280,3 +280,40 @@ def test_split_planes_ragged_against_oracle():
     assert wsb > 0
     assert R.rel_error(c, ref) <= 5e-6
     assert R.rel_error(c, exp3) <= 2e-6
+
+
+# Leading dimensions at the planes path's 32-bit buffer-offset limit (a
+# K-contiguous plane is addressed one 128-row panel at a time, C 64 rows of ldc
+# at a time).  Just below it the planes path runs; just past it the call takes
+# the split-on-load kernel, whose addresses are 64-bit.  Operand and C storage
+# is 8 GiB each; only the M x K (N x K) block is set.
+@pytest.mark.parametrize("side", ["below", "past"])
+def test_split_leading_dimensions_at_the_32_bit_limit(side):
+    m, n, k = 128, 128, 256
+    ld = (1 << 24) - 64 if side == "below" else (1 << 24) + 64   # 128 * ld * 2 bytes vs 2^32
+    ldc = (1 << 24) - 64 if side == "below" else (1 << 24) + 64  # 64 * ldc * 4 bytes vs 2^32
+    a, bt = inputs.gemm_split(m, n, k)
+    exp3 = R.split_expansion(a, bt, "bf16")
+
+    def big(x):
+        s = torch.zeros((x.shape[0], ld), device=device())
+        s[:, : x.shape[1]] = dev32(x)
+        return s
+
+    say("split ld at 32-bit limit", side, ld, ldc)
+    da, db = big(a), big(bt)
+    wsb = mfl.gemm_split_fp32_workspace_bytes(m, n, k, ld, mfl.ROW_MAJOR, mfl.SPLIT, ld, mfl.COL_MAJOR, mfl.SPLIT, ldc)
+    assert (wsb > 0) == (side == "below")
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=device())
+    c = torch.full((m, ldc), 12345.0, device=device())
+    c[:, :n] = np.nan
+    mfl.gemm_split_fp32_ws(mfl.BF16, m, n, k, da, ld, mfl.ROW_MAJOR, mfl.SPLIT, db, ld, mfl.COL_MAJOR, mfl.SPLIT, 3, 0,
+                           c, ldc, 0, ws, max(wsb, 256), stream())
+    out = host(c[:, :n])
+    assert not np.isnan(out).any()
+    assert R.rel_error(out, exp3) <= 2e-6
+    assert bool((c[:, n:] == 12345.0).all()), "padding of C was written"
+    compact = run_split(a, bt, 3)
+    assert np.array_equal(out.view(np.uint32), compact.view(np.uint32))
+    del da, db, ws, c
+    torch.cuda.empty_cache()
