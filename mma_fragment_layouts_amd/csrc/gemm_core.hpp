@@ -287,6 +287,81 @@ __device__ __forceinline__ void mma_slab_carry(const uint16_t* sA, const uint16_
   }
 }
 
+// mma_slab / mma_slab_carry calling `after_reads()` once every fragment read
+// of the slab is issued (before the last MFMA K step's MFMAs), for a caller
+// that must not issue its next direct-to-LDS loads ahead of those reads.  Kept
+// apart from the plain forms, whose code the extra parameter would perturb.
+template <int SHAPE, int DT, int TM, int TN, int BK, bool MASKK, class RA, class RB, class Hook>
+__device__ __forceinline__ void mma_slab_then(const uint16_t* sA, const uint16_t* sB, const RA& fa, const RB& fb,
+                                              typename Shape<SHAPE>::Acc (&acc)[TM][TN], int kvalid,
+                                              const Hook& after_reads) {
+  constexpr int MN = Shape<SHAPE>::MN, KM = Shape<SHAPE>::K, KS = BK / KM;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    u32x4 a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = frag_read(sA, fa, kk, i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = frag_read(sB, fb, kk, j);
+    if (kk == KS - 1) after_reads();
+    if constexpr (MASKK) {
+      if (kvalid < BK && kk * KM + 8 * ((int)(threadIdx.x & 63) / MN) >= kvalid) {  // kvalid is wave-uniform
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[j] = u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma<SHAPE, DT>(a[i], b[j], acc[i][j]);
+  }
+}
+
+template <int SHAPE, int DT, int TM, int TN, int BK, int CARRY, bool MASKK, class RA, class RB, class Hook>
+__device__ __forceinline__ void mma_slab_carry_then(const uint16_t* sA, const uint16_t* sB, const RA& fa,
+                                                    const RB& fb, typename Shape<SHAPE>::Acc (&acc)[TM][TN],
+                                                    u32x4 (&ca)[CARRY], u32x4 (&cb)[TN], bool pending, int kvalid,
+                                                    const Hook& after_reads) {
+  constexpr int MN = Shape<SHAPE>::MN, KM = Shape<SHAPE>::K, KS = BK / KM;
+  static_assert(CARRY > 0 && CARRY < TM, "carry some but not all fragment rows");
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    u32x4 a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = frag_read(sA, fa, kk, i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = frag_read(sB, fb, kk, j);
+    if (kk == KS - 1) after_reads();
+    if constexpr (MASKK) {
+      if (kvalid < BK && kk * KM + 8 * ((int)(threadIdx.x & 63) / MN) >= kvalid) {  // kvalid is wave-uniform
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[j] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (kk == 0 && pending) {
+#pragma unroll
+      for (int c = 0; c < CARRY; ++c) asm volatile("" : "+v"(ca[c]));
+      mma_carried<SHAPE, DT, TM, TN, CARRY>(ca, cb, acc);
+    }
+    constexpr int last = KS - 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      if (kk != last || i < TM - CARRY)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma<SHAPE, DT>(a[i], b[j], acc[i][j]);
+    if (kk == last) {
+#pragma unroll
+      for (int c = 0; c < CARRY; ++c) ca[c] = a[TM - CARRY + c];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) cb[j] = b[j];
+    }
+  }
+}
+
 // Wait until at most N of this wave's vector-memory operations (the
 // direct-to-LDS loads included) are outstanding.
 template <int N>

@@ -76,16 +76,24 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
   for (int ch = 0; ch < P::CHAINS; ++ch) zero_acc<SHAPE, TM, TN>(acc[ch]);
 
   const int KT = (K + BK - 1) / BK;  // a multiple of BK unless EDGE
+  // With a k-major plane the next stage is requested after this stage's last
+  // fragment reads: the compiler makes an LDS transpose read that follows a
+  // direct-to-LDS load wait for it (it cannot tell the buffers apart), which
+  // would expose the load latency in every K step.
+  constexpr bool LATE = AKM || BKM;
+  constexpr int KS = BK / Shape<SHAPE>::K;
   if (KT > 0) issue(0, 0);
   for (int kt = 0; kt < KT; ++kt) {
     // this wave's loads of stage kt have landed; after the barrier every
     // wave's have, and stage kt-1 (the buffer refilled next) is retired
     wait_vmcnt<0>();
     __syncthreads();
-    if (kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * BK);
+    if constexpr (!LATE) {
+      if (kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * BK);
+    }
     const uint16_t* st = lds + (kt & 1) * STAGE;
 #pragma unroll
-    for (int kk = 0; kk < BK / Shape<SHAPE>::K; ++kk) {
+    for (int kk = 0; kk < KS; ++kk) {
       u32x4 ah[TM], al[TM], bh[TN], bl[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -96,6 +104,9 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
       for (int j = 0; j < TN; ++j) {
         bh[j] = frag_read(st + 2 * PLANE, fb, kk, j);
         bl[j] = frag_read(st + 3 * PLANE, fb, kk, j);
+      }
+      if constexpr (LATE) {
+        if (kk == KS - 1 && kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * BK);
       }
       if constexpr (EDGE) {
         // K positions 8*(lane/16) .. +7 of MFMA step kk (the operand numeral);

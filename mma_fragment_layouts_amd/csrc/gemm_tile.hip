@@ -141,6 +141,16 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
   u32x4 ca[CARRY > 0 ? CARRY : 1], cb[TN];  // fragments of the MFMAs carried over a barrier
 
   const int KT = (K + BK - 1) / BK;  // a multiple of BK unless EDGE
+  // With a k-major operand the next stage's loads are issued after this
+  // stage's last fragment reads: the compiler makes an LDS transpose read
+  // that follows a direct-to-LDS load wait for that load to land (it cannot
+  // tell the two buffers apart), which issued right after the barrier would
+  // expose the whole load latency in every K step.  Measured at 4096^3 bf16:
+  // row-major B 113.4 -> 110.7 us, both k-major 123.5 -> 114.8 us, and 2.7-4.5 %
+  // for every k-major order with the 32x32x16 instruction; column-major A
+  // alone with 16x16x32 ran slower issued late (115.2 -> 125.2 us) and keeps
+  // the early issue.
+  constexpr bool LATE = (AKM || BKM) && !(SHAPE == 0 && AKM && !BKM);
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
     if (st < KT) issue(st, st * BK);
@@ -152,13 +162,25 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
     else
       wait_vmcnt<0>();
     __syncthreads();
-    if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
-    const int cur = (kt % STAGES) * STAGE;
-    if constexpr (CARRY > 0)
-      mma_slab_carry<SHAPE, DT, TM, TN, BK, CARRY, EDGE>(lds + cur, lds + cur + BM * BK, fa, fb, acc, ca, cb, kt > 0,
-                                                          K - kt * BK);
-    else
-      mma_slab<SHAPE, DT, TM, TN, BK, EDGE>(lds + cur, lds + cur + BM * BK, fa, fb, acc, K - kt * BK);
+    if constexpr (!LATE) {
+      if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
+      const int cur = (kt % STAGES) * STAGE;
+      if constexpr (CARRY > 0)
+        mma_slab_carry<SHAPE, DT, TM, TN, BK, CARRY, EDGE>(lds + cur, lds + cur + BM * BK, fa, fb, acc, ca, cb,
+                                                            kt > 0, K - kt * BK);
+      else
+        mma_slab<SHAPE, DT, TM, TN, BK, EDGE>(lds + cur, lds + cur + BM * BK, fa, fb, acc, K - kt * BK);
+    } else {
+      const int cur = (kt % STAGES) * STAGE;
+      const auto late = [&] {
+        if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
+      };
+      if constexpr (CARRY > 0)
+        mma_slab_carry_then<SHAPE, DT, TM, TN, BK, CARRY, EDGE>(lds + cur, lds + cur + BM * BK, fa, fb, acc, ca, cb,
+                                                                 kt > 0, K - kt * BK, late);
+      else
+        mma_slab_then<SHAPE, DT, TM, TN, BK, EDGE>(lds + cur, lds + cur + BM * BK, fa, fb, acc, K - kt * BK, late);
+    }
   }
   if constexpr (CARRY > 0)
     if (KT > 0) mma_carried<SHAPE, DT, TM, TN, CARRY>(ca, cb, acc);
