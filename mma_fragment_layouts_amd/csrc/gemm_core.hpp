@@ -287,10 +287,11 @@ __device__ __forceinline__ void mma_slab_carry(const uint16_t* sA, const uint16_
   }
 }
 
-// mma_slab / mma_slab_carry calling `after_reads()` once every fragment read
-// of the slab is issued (before the last MFMA K step's MFMAs), for a caller
-// that must not issue its next direct-to-LDS loads ahead of those reads.  Kept
-// apart from the plain forms, whose code the extra parameter would perturb.
+// mma_slab / mma_slab_carry calling `after_reads()` once the fragment reads of
+// the slab's first MFMA K step are issued (before that step's MFMAs), for a
+// caller that must not issue its next direct-to-LDS loads ahead of those
+// reads.  Kept apart from the plain forms, whose code the extra parameter
+// would perturb.
 template <int SHAPE, int DT, int TM, int TN, int BK, bool MASKK, class RA, class RB, class Hook>
 __device__ __forceinline__ void mma_slab_then(const uint16_t* sA, const uint16_t* sB, const RA& fa, const RB& fb,
                                               typename Shape<SHAPE>::Acc (&acc)[TM][TN], int kvalid,
@@ -303,7 +304,7 @@ __device__ __forceinline__ void mma_slab_then(const uint16_t* sA, const uint16_t
     for (int i = 0; i < TM; ++i) a[i] = frag_read(sA, fa, kk, i);
 #pragma unroll
     for (int j = 0; j < TN; ++j) b[j] = frag_read(sB, fb, kk, j);
-    if (kk == KS - 1) after_reads();
+    if (kk == 0) after_reads();
     if constexpr (MASKK) {
       if (kvalid < BK && kk * KM + 8 * ((int)(threadIdx.x & 63) / MN) >= kvalid) {  // kvalid is wave-uniform
 #pragma unroll
@@ -333,7 +334,7 @@ __device__ __forceinline__ void mma_slab_carry_then(const uint16_t* sA, const ui
     for (int i = 0; i < TM; ++i) a[i] = frag_read(sA, fa, kk, i);
 #pragma unroll
     for (int j = 0; j < TN; ++j) b[j] = frag_read(sB, fb, kk, j);
-    if (kk == KS - 1) after_reads();
+    if (kk == 0) after_reads();
     if constexpr (MASKK) {
       if (kvalid < BK && kk * KM + 8 * ((int)(threadIdx.x & 63) / MN) >= kvalid) {  // kvalid is wave-uniform
 #pragma unroll

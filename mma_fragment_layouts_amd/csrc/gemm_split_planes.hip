@@ -76,10 +76,11 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
   for (int ch = 0; ch < P::CHAINS; ++ch) zero_acc<SHAPE, TM, TN>(acc[ch]);
 
   const int KT = (K + BK - 1) / BK;  // a multiple of BK unless EDGE
-  // With a k-major plane the next stage is requested after this stage's last
-  // fragment reads: the compiler makes an LDS transpose read that follows a
-  // direct-to-LDS load wait for it (it cannot tell the buffers apart), which
-  // would expose the load latency in every K step.
+  // With a k-major plane the next stage is requested after the fragment reads
+  // of this stage's first MFMA K step: the compiler makes an LDS transpose
+  // read that follows a direct-to-LDS load wait for it (it cannot tell the
+  // buffers apart), which would hold up the step's first reads for the whole
+  // load latency.
   constexpr bool LATE = AKM || BKM;
   constexpr int KS = BK / Shape<SHAPE>::K;
   if (KT > 0) issue(0, 0);
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(512) void gemm_split_planes_kernel(const uint16_t* 
         bl[j] = frag_read(st + 3 * PLANE, fb, kk, j);
       }
       if constexpr (LATE) {
-        if (kk == KS - 1 && kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * BK);
+        if (kk == 0 && kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * BK);
       }
       if constexpr (EDGE) {
         // K positions 8*(lane/16) .. +7 of MFMA step kk (the operand numeral);

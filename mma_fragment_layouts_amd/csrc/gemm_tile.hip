@@ -141,16 +141,13 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
   u32x4 ca[CARRY > 0 ? CARRY : 1], cb[TN];  // fragments of the MFMAs carried over a barrier
 
   const int KT = (K + BK - 1) / BK;  // a multiple of BK unless EDGE
-  // With a k-major operand the next stage's loads are issued after this
-  // stage's last fragment reads: the compiler makes an LDS transpose read
-  // that follows a direct-to-LDS load wait for that load to land (it cannot
-  // tell the two buffers apart), which issued right after the barrier would
-  // expose the whole load latency in every K step.  Measured at 4096^3 bf16:
-  // row-major B 113.4 -> 110.7 us, both k-major 123.5 -> 114.8 us, and 2.7-4.5 %
-  // for every k-major order with the 32x32x16 instruction; column-major A
-  // alone with 16x16x32 ran slower issued late (115.2 -> 125.2 us) and keeps
-  // the early issue.
-  constexpr bool LATE = (AKM || BKM) && !(SHAPE == 0 && AKM && !BKM);
+  // With a k-major operand the next stage's loads are issued after the
+  // fragment reads of this stage's first MFMA K step: the compiler makes an
+  // LDS transpose read that follows a direct-to-LDS load wait for that load to
+  // land (it cannot tell the two buffers apart), so loads issued right after
+  // the barrier would hold up the step's first reads for their whole latency.
+  // Issued there, they still have most of the step to land.
+  constexpr bool LATE = AKM || BKM;
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
     if (st < KT) issue(st, st * BK);
