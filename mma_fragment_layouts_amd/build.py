@@ -30,19 +30,14 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators and results in the architectural VGPRs.  Left to itself
+    # the compiler splits a large accumulator set between VGPRs and AGPRs and
+    # copies it back and forth around the MFMAs (hundreds of v_accvgpr moves per
+    # loop in the 128 x 128 GEMM tiles and the block-repeat tiles); with this form
+    # the 128 x 128 block-repeat kernel runs 28 % faster and the 64 x 64 ones
+    # 13-22 %, and kernels whose registers fit either way compile to the same code.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
-
-# MFMA accumulators and results in the architectural VGPRs.  Left to itself the
-# compiler splits a large accumulator set between VGPRs and AGPRs and copies it
-# back and forth around the MFMAs (hundreds of v_accvgpr moves per loop in the
-# 128 x 128 GEMM tiles and the block-repeat tiles); with this form the 128 x 128
-# block-repeat kernel runs 28 % faster and the 64 x 64 ones 13-22 %, and kernels
-# whose registers fit either way compile to the same code.  The split-on-load
-# GEMMs (split_*_k[cs].hip) keep the default: with two or three accumulator
-# chains they need more than the 256 VGPRs, the overflow lands in AGPRs as
-# copies again, and with the flag they run 4-11 % slower.
-VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-DEFAULT_FORM = {"split_bf16_kc.hip", "split_bf16_ks.hip", "split_f16_kc.hip", "split_f16_ks.hip"}
 
 
 OBJ_SAN = os.path.join(HERE, "_build_san")
@@ -66,8 +61,6 @@ def sources():
 def _compile(src: str, sanitize: bool = False) -> str:
     obj = os.path.join(OBJ_SAN if sanitize else OBJ, os.path.basename(src)[:-4] + ".o")
     flags = [f for f in FLAGS if f != "-O3"] + SAN_FLAGS if sanitize else FLAGS
-    if os.path.basename(src) not in DEFAULT_FORM:
-        flags = flags + VGPR_FORM
     cmd = [HIPCC, *flags, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
