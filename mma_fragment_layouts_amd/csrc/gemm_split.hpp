@@ -223,13 +223,14 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_split_kernel(const float* 
 }
 
 // Launch helper used by the C ABI and by the attention pair.
-// 128 x 128 tiles, 8 waves of 64 x 32 (two per SIMD; the whole tile's two
-// LDS stages take 128 KiB, so one workgroup per CU): at 4096^3 with 3 chains
-// 429 us against 522 us for 4 waves of 64 x 64, bit-identical.
+// 128 x 128 tiles, 16 waves of 32 x 32 (four per SIMD; the tile's two LDS
+// stages take 128 KiB, so one workgroup per CU): at 4096^3 with 3 chains
+// 410 us against 439 us for 8 waves of 64 x 32 and 522 us for 4 of 64 x 64,
+// bit-identical.
 template <int DT, class P, bool AK, bool BKC>
 inline int launch_split(const float* a, int64_t lda, const float* b, int64_t ldb, float* c, int64_t ldc, int M, int N,
                         int K, int splits, int k_per_split, int64_t c_split_stride, int accumulate, hipStream_t s) {
-  constexpr int BM = 128, BN = 128, WGM = 2, WGN = 4;
+  constexpr int BM = 128, BN = 128, WGM = 4, WGN = 4;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const dim3 grid(tiles_m * tiles_n, splits), block(WGM * WGN * 64);
   if constexpr (AK && BKC) {
