@@ -227,7 +227,7 @@ MFL_API int split_fp32(int dtype, const float *x, void *hi, void *lo, int64_t n,
  * orders.  The tile follows the problem size: 256 x 256 when that gives at
  * least 128 workgroups (192 x 192 instead, for K-contiguous operands, when
  * 256-tiles would fill only part of one round of one tile per compute unit
- * and 192-tiles fit in one), else 128 x 128 or 64 x 64; every output element
+ * and 192-tiles fit in one), else 128 x 128, 64 x 64 or 32 x 32; every output element
  * sees the same MFMA sequence whatever the tile, so the bits do not depend on
  * it.  A size whose 256 x 256 tiles fill at least two whole rounds of
  * one tile per compute unit plus a partial one runs as two launches on the

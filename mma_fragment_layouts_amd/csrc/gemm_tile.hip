@@ -260,10 +260,10 @@ static int dispatch_fast(int shape, const void* a, int64_t lda, const void* b, i
                          int M, int N, int K, int accumulate, hipStream_t s) {
   // The largest tile that still gives the chip at least 128 workgroups:
   // 256 x 256 (16 waves of 64 x 64; 192 x 192 when that fills one round
-  // better, below), 128 x 128 (4 waves of 64 x 64), or for
-  // small problems with K-contiguous operands 64 x 64 (2 waves of 32 x 64),
-  // where a single big tile would leave all but a few CUs idle.  Sizes that
-  // are not tile multiples run the EDGE variant of the same kernel.
+  // better, below), 128 x 128 (4 waves of 64 x 64), or for small problems
+  // with K-contiguous operands 64 x 64 or 32 x 32 (4 waves each, below), where
+  // a single big tile would leave all but a few CUs idle.  Sizes that are not
+  // tile multiples run the EDGE variant of the same kernel.
   const auto count = [&](int t) { return (int64_t)((M + t - 1) / t) * ((N + t - 1) / t); };
   const bool s32 = shape == MFL_MFMA_32X32X16;
   if (const int m1 = quantisation_split_rows(M, N)) {
@@ -292,9 +292,17 @@ static int dispatch_fast(int shape, const void* a, int64_t lda, const void* b, i
   if (count(128) >= 128 || AKM || BKM)
     return s32 ? launch_fast<128, 128, 2, 2, 1, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)
                : launch_fast<128, 128, 2, 2, 0, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-  if constexpr (!AKM && !BKM)
-    return s32 ? launch_fast<64, 64, 2, 1, 1, DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)
-               : launch_fast<64, 64, 2, 1, 0, DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  // Small problems: 64 x 64 tiles with 4 waves of 32 x 32, or, with the
+  // 16x16x32 instruction, 32 x 32 tiles (4 waves of 16 x 16) when 64-tiles
+  // would give fewer than 128 workgroups.  Measured (bf16, kernel time): 1024^3
+  // 6.7 us against 7.4 us for 64 x 64 tiles with 2 waves; 512^3 3.8 us on
+  // 32 x 32 tiles against 4.2 / 4.7 us on 64 x 64 tiles with 4 / 2 waves.
+  if constexpr (!AKM && !BKM) {
+    if (s32) return launch_fast<64, 64, 2, 2, 1, DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+    if (count(64) >= 128)
+      return launch_fast<64, 64, 2, 2, 0, DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+    return launch_fast<32, 32, 2, 2, 0, DT, false, false>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  }
   return MFL_EUNSUPPORTED;  // not reached: k-major operands always take a 128 or 256 tile
 }
 

@@ -182,8 +182,9 @@ def test_dense_4096_full(shape, fmt):
 # instructions and both 16-bit types; accumulate on for one of each.
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", [0, 1])
-@pytest.mark.parametrize("mnk,accumulate", [((256, 256, 256), 0),     # 64 x 64, 16 workgroups
-                                             ((192, 320, 128), 1),     # 64 x 64 (not a multiple of 128)
+@pytest.mark.parametrize("mnk,accumulate", [((256, 256, 256), 0),     # 32 x 32 (64 x 64 with 32x32x16)
+                                             ((192, 320, 128), 1),     # 32 x 32, ragged for 64 and 128
+                                             ((512, 768, 256), 0),     # 32 x 32, 384 workgroups
                                              ((1024, 1024, 512), 0),   # 64 x 64, 256 workgroups
                                              ((2048, 2048, 256), 1),   # 128 x 128, 256 workgroups
                                              ((2048, 4096, 128), 0),   # 256 x 256, 128 workgroups
@@ -215,7 +216,7 @@ ORDERS = [(mfl.ROW_MAJOR, mfl.COL_MAJOR), (mfl.ROW_MAJOR, mfl.ROW_MAJOR), (mfl.C
 @pytest.mark.parametrize("mnk,accumulate", [((4096, 4096, 128), 0),   # 256 x 256 tiles
                                             ((2048, 1024, 192), 0),   # 128 x 128 tiles
                                             ((3072, 3072, 256), 1),   # 192 x 192 (K-contiguous, 16x16x32), 256 x 256
-                                            ((256, 384, 320), 1),     # 128 x 128 (k-major), 64 x 64 (K-contiguous)
+                                            ((256, 384, 320), 1),     # 128 x 128 (k-major), 32 x 32 (K-contiguous)
                                             ((128, 128, 64), 0)])     # one tile, one K step
 def test_fast_path_all_orders_bit_identical(mnk, accumulate, shape, fmt):
     m, n, k = mnk
@@ -269,7 +270,7 @@ def test_dense_4096_bf16_other_orders(orders, shape):
 # ldc = N + 5 with a sentinel in its padding, which must survive; every order
 # must still give the same bits.
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
-@pytest.mark.parametrize("mnk,accumulate", [((200, 136, 128), 0),      # 64 x 64 tiles (K-contiguous), 128 (k-major)
+@pytest.mark.parametrize("mnk,accumulate", [((200, 136, 128), 0),      # 32 x 32 tiles (K-contiguous), 128 (k-major)
                                             ((1000, 520, 192), 1),
                                             ((8, 264, 64), 0),         # fewer rows than one tile
                                             ((4000, 4000, 256), 0),    # 256 x 256 tiles, ragged last row / column

@@ -2,7 +2,7 @@
 
 These run on the CPU and check the design's index arithmetic for the
 configurations the fast paths launch (dense GEMM: 256 x 256 tiles with 4 x 4
-waves, 192 x 192 with 3 x 4, 128 x 128 with 2 x 2, 64 x 64 with 2 x 1; split GEMM planes kernel:
+waves, 192 x 192 with 3 x 4, 128 x 128, 64 x 64 and 32 x 32 with 2 x 2; split GEMM planes kernel:
 128 x 128 with 4 x 4) at tile-multiple and ragged sizes:
 
   * the XCD-aware tile order (``tile_of`` in csrc/common.hpp) visits every
@@ -25,7 +25,7 @@ import pytest
 import mma_fragment_layouts_amd as mfl
 
 # (BM, BN, WGM, WGN): the dense fast path's launches and the split planes kernel's
-CONFIGS = [(256, 256, 4, 4), (192, 192, 3, 4), (128, 128, 2, 2), (64, 64, 2, 1), (128, 128, 4, 4)]
+CONFIGS = [(256, 256, 4, 4), (192, 192, 3, 4), (128, 128, 2, 2), (64, 64, 2, 2), (32, 32, 2, 2), (128, 128, 4, 4)]
 RAGGED = [(4096, 4096), (4000, 4000), (1000, 520), (300, 1000), (257, 129), (64, 64), (1, 1)]
 
 
@@ -123,7 +123,7 @@ def test_epilogue_stores_each_element_once(m, n, shape):
     mn = mfl.mfl_acc_info(shape)[2]
     for bm, bn, wgm, wgn in CONFIGS:
         if (bm // wgm) % mn or (bn // wgn) % mn:
-            continue   # 48-wide wave tiles: 16x16x32 only, as the dispatcher launches them
+            continue   # 48- and 16-wide wave tiles: 16x16x32 only, as the dispatcher launches them
         s = stored_elements(m, n, ldc, bm, bn, wgm, wgn, shape)
         assert len(s) == m * n, (bm, bn)
         assert len(set(s)) == m * n
