@@ -333,7 +333,8 @@ MFL_API int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int alg
  * `chains` (1 or 2) selects single-chain or separate hi/lo accumulators for
  * both products.  No causal mask and no 1/sqrt(d) scaling are applied.
  *   algo 0: the four steps as separate kernels, S and P~ materialised in the
- *           workspace (split GEMM, row softmax, split-K split GEMM, reduce);
+ *           workspace (scores per 128 queries and key slice, row softmax,
+ *           P~ V per key slice, fixed-order reduce of the slices);
  *   algo 1: fused — per 128 queries and key slice, both products and an online
  *           softmax (running max, rescaled accumulators) stay in registers and
  *           LDS; key slices are merged by their exp(m_s - m) weights;

@@ -3,10 +3,9 @@
 // attention_fused.hip ("What's going on": q is split for q.k, p is split for p.v, each into an
 // FP16 hi and lo half; "The fix": hi and lo products in separate accumulators).
 //
-//   1. S = Q K^T           split GEMM, Q split into f16 hi/lo, K rounded once
+//   1. S = Q K^T           Q split into f16 hi/lo, K rounded once
 //   2. m = rowmax S, P~ = exp(S - m), l = rowsum P~          (fp32, in place)
-//   3. O_s = P~[:, slice s] V[slice s, :]   split GEMM over K slices, P~ split,
-//                                           V rounded once
+//   3. O_s = P~[:, slice s] V[slice s, :]   per key slice, P~ split, V rounded once
 //   4. O = (sum_s O_s) / l  slices summed in a fixed order
 //
 // Normalisation is deferred to step 4: P~ lies in (0, 1] with its maximum
@@ -14,10 +13,18 @@
 // fp16's subnormal range and lose most of their lo half.  softmax(S) V equals
 // (P~ V) / l exactly in real arithmetic.  This version materialises S / P~ in
 // the caller's workspace (HBM-bound); it keeps every step on the device.
+//
+// Kernels: attn_prep_kvt rounds K into K16 (key-major) and V into V16T (one
+// row of nk keys per dim); attn_scores computes S for 128 queries and one key
+// slice, Q's hi/lo halves held in registers and K16 chunks of 64 keys streamed
+// through LDS; the row softmax reads each row once and rewrites it; attn_pv
+// streams P~ and V16T chunks through LDS.  S and P~ are stored chunk-blocked,
+// S[key / 64][q][key % 64]: the 128 queries x 64 keys a workgroup handles per
+// chunk are 32 KiB of contiguous memory, written and read whole.
+#include <algorithm>
 #include <mutex>
 
 #include "attention_fused.hpp"
-#include "gemm_split.hpp"
 
 namespace mfl {
 
@@ -31,6 +38,11 @@ constexpr int kSoftmaxThreads = 512;
 constexpr int kSoftmaxVec = 16;  // f32x4 per thread: rows up to 32768 stay in registers
 // P~ = exp(s - m) is taken as 2^((s - m) log2 e) with the hardware exp2.
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Element (q, key) of the chunk-blocked nq x nk layout.
+__device__ __forceinline__ int64_t blk_index(int64_t nq, int q, int64_t key) {
+  return ((key >> 6) * nq + q) * kAttnKV + (key & 63);
+}
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -57,22 +69,173 @@ __device__ __forceinline__ float block_reduce(float x, float* red) {
   return r;
 }
 
-// One workgroup per row; the row (n <= 32768, n % 4 == 0) is read once into
-// registers (non-temporal loads: S is not read again), P~ written back in
-// place, m and l written per row.  The row sum adds each thread's values in
-// order, then the threads' partial sums.
-__global__ __launch_bounds__(kSoftmaxThreads) void softmax_rows_regs(float* __restrict__ S, int64_t lds_, int n,
+// K16 = RNE16(K), key-major like K; V16T = RNE16(V) transposed, V16T[d][key].
+// One workgroup per 64 keys: each thread rounds 32 consecutive values of the
+// K block, and one pair of keys x 16 dims of the V block, whose halves it
+// packs per dim into 32-bit words of an LDS tile (a dim row of 32 key pairs,
+// padded to 33 words); the tile leaves as 128-byte rows of V16T.
+__global__ __launch_bounds__(256) void attn_prep_kvt(const float* __restrict__ K, const float* __restrict__ V,
+                                                    uint16_t* __restrict__ Kq, uint16_t* __restrict__ VqT, int64_t nk) {
+  constexpr int PADW = 33;
+  __shared__ uint32_t t[kAttnD * PADW];
+  const int64_t key0 = (int64_t)blockIdx.x * kAttnKV;
+  const int tid = threadIdx.x;
+  {
+    const int64_t base = key0 * kAttnD + tid * 32;
+    uint32_t w[16];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(K + base + 4 * q);
+      const Split2 a = split2(x[0], x[1]), b = split2(x[2], x[3]);
+      w[2 * q] = a.hi;
+      w[2 * q + 1] = b.hi;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x4 o;
+      __builtin_memcpy(&o, w + 4 * q, 16);
+      *reinterpret_cast<u32x4*>(Kq + base + 8 * q) = o;
+    }
+  }
+  {
+    const int kp = tid >> 3, d0 = (tid & 7) * 16;
+    const float* r0 = V + (key0 + 2 * kp) * kAttnD + d0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(r0 + 4 * q);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(r0 + kAttnD + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[(d0 + 4 * q + e) * PADW + kp] = split2(a[e], b[e]).hi;  // keys 2kp | 2kp+1
+    }
+  }
+  __syncthreads();
+  const int d = tid >> 1, h = tid & 1;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t* r = t + d * PADW + 16 * h + 4 * q;
+    *reinterpret_cast<u32x4*>(VqT + d * nk + key0 + 32 * h + 8 * q) = u32x4{r[0], r[1], r[2], r[3]};
+  }
+}
+
+// Keys [kbeg, kbeg + 64 * nchunks) of slice sp: slices of kps keys, the last
+// one shorter when nk is not a multiple of kps.
+__device__ __forceinline__ int slice_chunks(int sp, int kps, int64_t nk) {
+  const int64_t kbeg = (int64_t)sp * kps;
+  return (int)((min(nk, kbeg + kps) - kbeg) / kAttnKV);
+}
+
+// Step 1: S (chunk-blocked) for 128 queries (8 waves x 16) and one key slice.
+// Each wave holds the B fragments of its 16 queries' hi and lo halves for the
+// whole slice; per 64-key chunk it computes S^T (64 keys x 16 queries) =
+// K16 . Q^T with the hi products in one chain and the lo products in a second
+// (CHAINS == 2) or the same one, adds the chains in fp32 and stores the tile.
+// K16 chunks arrive by direct-to-LDS loads, two stages.
+template <int CHAINS>
+__global__ __launch_bounds__(512) void attn_scores(const float* __restrict__ Q, const uint16_t* __restrict__ Kq,
+                                                   float* __restrict__ S, int nq, int64_t nk, int kps, int qblocks,
+                                                   int xcd_map) {
+  constexpr int BK = 64, KT = kAttnKV * BK, STAGE = 2 * KT, NW = 8, LOADS = 2;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
+  int qb, sp;
+  attn_block_of(blockIdx.x, gridDim.x, qblocks, xcd_map, qb, sp);
+  const int64_t kbeg = (int64_t)sp * kps;
+  const int nchunks = slice_chunks(sp, kps, nk);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, g = lane >> 4;
+  const int qw = qb * kAttnQ + wave * 16;
+  // Q^T fragments: lane supplies query qw + lr, dims 32*d + 8*g .. +7
+  u32x4 qh[4], ql[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float* p = Q + (int64_t)(qw + lr) * kAttnD + 32 * d + 8 * g;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(p), x1 = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const Split2 s0 = split2(x0[2 * e], x0[2 * e + 1]);
+      const Split2 s1 = split2(x1[2 * e], x1[2 * e + 1]);
+      qh[d][e] = s0.hi;
+      ql[d][e] = s0.lo;
+      qh[d][2 + e] = s1.hi;
+      ql[d][2 + e] = s1.lo;
+    }
+  }
+  // Stage fill: 16 wave loads of 1 KiB, block b = wave + 8i: K16 half b / 8
+  // (dims 64 (b / 8) ..), key rows 8 (b % 8) .. +7 (128 bytes each, chunk
+  // lane % 8 of row 8 (b % 8) + lane / 8 receives logical chunk
+  // (lane % 8) ^ swz(row)).
+  uint32_t voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int b = wave + NW * i;
+    const int row = 8 * (b & 7) + (lane >> 3);
+    voff[i] = (uint32_t)(row * kAttnD + 64 * (b >> 3) + (((lane & 7) ^ swz<BK>(row)) * 8)) * 2u;
+  }
+  auto issue = [&](int chunk) {
+    const rsrc_t rk = make_rsrc(Kq + (kbeg + (int64_t)chunk * kAttnKV) * kAttnD, kAttnKV * kAttnD * 2);
+    uint16_t* base = lds + (chunk & 1) * STAGE;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(base + i * KT + wave * 8 * BK), 16, voff[i], 0, 0, 0);
+    asm volatile("" ::: "memory");  // the loads stay ahead of the chunk's score stores
+  };
+  const FragOffsets<0, BK> fo(0, lane);
+  // lane's keys 16 kt + 4 g .. +3 of each chunk, query qw + lr
+  float* srow = S + ((kbeg >> 6) * nq + qw + lr) * kAttnKV + 4 * g;
+  const int64_t cstride = (int64_t)nq * kAttnKV;
+  issue(0);
+  for (int c = 0; c < nchunks; ++c) {
+    // chunk c's loads were issued before chunk c-1's four score stores
+    if (c > 0)
+      wait_vmcnt<4>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    if (c + 1 < nchunks) issue(c + 1);
+    const uint16_t* st = lds + (c & 1) * STAGE;
+    f32x4 sh[4], sl[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      sh[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sl[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      u32x4 a[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) a[kt] = lds_read16(st + (d >> 1) * KT, fo.off[d & 1] + kt * 16 * BK);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        sh[kt] = mfma<0, MFL_F16>(a[kt], qh[d], sh[kt]);
+        f32x4& corr = CHAINS == 2 ? sl[kt] : sh[kt];
+        corr = mfma<0, MFL_F16>(a[kt], ql[d], corr);
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4 s = sh[kt];
+      if constexpr (CHAINS == 2) s = s + sl[kt];
+      *reinterpret_cast<f32x4*>(srow + c * cstride + 16 * kt) = s;
+    }
+  }
+}
+
+// Step 2, one workgroup per row (chunk-blocked layout; n <= 32768): the row is
+// read once into registers, P~ written back in place, m and l written per row.
+// Thread t holds the values at columns 4 (512 i + t) .. +3; the row sum adds
+// each thread's values in order, then the threads' partial sums.
+__global__ __launch_bounds__(kSoftmaxThreads) void softmax_rows_regs(float* __restrict__ S, int nq, int n,
                                                                    float* __restrict__ m_out,
                                                                    float* __restrict__ l_out) {
   __shared__ float red[kSoftmaxThreads / 64];
-  float* row = S + (int64_t)blockIdx.x * lds_;
+  const int q = blockIdx.x;
   f32x4 v[kSoftmaxVec];
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kSoftmaxVec; ++i) {
     const int c = (i * kSoftmaxThreads + threadIdx.x) * 4;
     if (c < n) {
-      v[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + c));
+      v[i] = *reinterpret_cast<const f32x4*>(S + blk_index(nq, q, c));
       mx = fmaxf(mx, fmaxf(fmaxf(v[i][0], v[i][1]), fmaxf(v[i][2], v[i][3])));
     }
   }
@@ -88,75 +251,181 @@ __global__ __launch_bounds__(kSoftmaxThreads) void softmax_rows_regs(float* __re
         p[e] = __builtin_amdgcn_exp2f((v[i][e] - mx) * kLog2e);
         sum += p[e];
       }
-      *reinterpret_cast<f32x4*>(row + c) = p;
+      *reinterpret_cast<f32x4*>(S + blk_index(nq, q, c)) = p;
     }
   }
   sum = block_reduce<false>(sum, red);
   if (threadIdx.x == 0) {
-    m_out[blockIdx.x] = mx;
-    l_out[blockIdx.x] = sum;
+    m_out[q] = mx;
+    l_out[q] = sum;
   }
 }
 
 // Rows longer than the register budget: one pass for the max, one for P~ and l.
-__global__ __launch_bounds__(kSoftmaxThreads) void softmax_rows_2pass(float* __restrict__ S, int64_t lds_, int n,
+__global__ __launch_bounds__(kSoftmaxThreads) void softmax_rows_2pass(float* __restrict__ S, int nq, int64_t n,
                                                                     float* __restrict__ m_out,
                                                                     float* __restrict__ l_out) {
   __shared__ float red[kSoftmaxThreads / 64];
-  float* row = S + (int64_t)blockIdx.x * lds_;
+  const int q = blockIdx.x;
   float mx = -INFINITY;
-  for (int c = threadIdx.x * 4; c < n; c += kSoftmaxThreads * 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(row + c);
+  for (int64_t c = threadIdx.x * 4; c < n; c += kSoftmaxThreads * 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(S + blk_index(nq, q, c));
     mx = fmaxf(mx, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
   }
   mx = block_reduce<true>(mx, red);
   float sum = 0.f;
-  for (int c = threadIdx.x * 4; c < n; c += kSoftmaxThreads * 4) {
-    f32x4 p = *reinterpret_cast<const f32x4*>(row + c);
+  for (int64_t c = threadIdx.x * 4; c < n; c += kSoftmaxThreads * 4) {
+    f32x4* p = reinterpret_cast<f32x4*>(S + blk_index(nq, q, c));
+    f32x4 x = *p;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      p[e] = __builtin_amdgcn_exp2f((p[e] - mx) * kLog2e);
-      sum += p[e];
+      x[e] = __builtin_amdgcn_exp2f((x[e] - mx) * kLog2e);
+      sum += x[e];
     }
-    *reinterpret_cast<f32x4*>(row + c) = p;
+    *p = x;
   }
   sum = block_reduce<false>(sum, red);
   if (threadIdx.x == 0) {
-    m_out[blockIdx.x] = mx;
-    l_out[blockIdx.x] = sum;
+    m_out[q] = mx;
+    l_out[q] = sum;
   }
 }
 
-// O[r][c] = (sum over slices s = 0, 1, ... of part[s][r][c]) / l[r].
+// Step 3 for 128 queries and one key slice: O_s^T (128 dims x 16 queries per
+// wave) += V16T . P~^T, the P~ fragments split into f16 hi (one chain) and lo
+// (a second chain, CHAINS == 2, or the same one).  Per 64-key chunk a stage
+// holds the V16T tile (128 dim rows of 64 keys, 128-byte rows swizzled like a
+// GEMM operand tile) and the chunk's P~ block (128 query rows of 64 fp32,
+// 256-byte rows whose 16-byte chunks are XOR-swizzled by row % 16, so that the
+// 16 rows one fragment read touches fall on distinct banks).  Three stages
+// of direct-to-LDS loads keep two chunks in flight.
+template <int CHAINS>
+__global__ __launch_bounds__(512) void attn_pv(const float* __restrict__ P, const uint16_t* __restrict__ VqT,
+                                               float* __restrict__ Opart, int nq, int64_t nk, int kps, int qblocks,
+                                               int xcd_map) {
+  constexpr int BK = 64, NST = 3, VST = kAttnD * BK, PST = kAttnQ * kAttnKV * 2;  // 16-bit elements
+  constexpr int STAGE = VST + PST, NW = 8, VL = 2, PL = 4, PER = VL + PL;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[NST * STAGE];
+  int qb, sp;
+  attn_block_of(blockIdx.x, gridDim.x, qblocks, xcd_map, qb, sp);
+  const int64_t kbeg = (int64_t)sp * kps;
+  const int nchunks = slice_chunks(sp, kps, nk);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, g = lane >> 4;
+  // wave load i fills V16T dim rows 8 (wave + 8i) .. +7 and P~ rows 4 (wave + 8i) .. +3
+  uint32_t voff[VL], poff[PL];
+#pragma unroll
+  for (int i = 0; i < VL; ++i) {
+    const int row = 8 * (wave + NW * i) + (lane >> 3);
+    voff[i] = (uint32_t)row * (uint32_t)nk * 2u + (uint32_t)(((lane & 7) ^ swz<BK>(row)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int row = 4 * (wave + NW * i) + (lane >> 4);
+    poff[i] = (uint32_t)row * 256u + (uint32_t)(((lane & 15) ^ (row & 15)) << 4);
+  }
+  // V16T from key key0 on: 127 rows of nk keys plus 64 keys (< 2^32 bytes for nk <= 2^24)
+  const uint32_t vbytes = (uint32_t)(((int64_t)(kAttnD - 1) * nk + kAttnKV) * 2);
+  auto fetch = [&](int chunk) {
+    uint16_t* base = lds + (chunk % NST) * STAGE;
+    const int64_t key0 = kbeg + (int64_t)chunk * kAttnKV;
+    const rsrc_t rv = make_rsrc(VqT + key0, vbytes);
+#pragma unroll
+    for (int i = 0; i < VL; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(base + (wave + NW * i) * 512), 16, voff[i], 0, 0, 0);
+    const rsrc_t rp = make_rsrc(P + ((key0 >> 6) * nq + qb * kAttnQ) * kAttnKV, PST * 2);
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_ptr_t)(base + VST + (wave + NW * i) * 512), 16, poff[i], 0, 0,
+                                               0);
+  };
+  const FragOffsets<0, BK> fo(0, lane);  // V16T fragments: dim row 16 i + lr, keys 32 t + 8 g ..
+  // P~ fragments: query row wave * 16 + lr, keys 32 t + 8 g .. +7 = logical
+  // 16-byte chunks 8 t + 2 g and 8 t + 2 g + 1 of the row
+  int pcol[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) pcol[t][h] = (wave * 16 + lr) * 128 + (((8 * t + 2 * g + h) ^ lr) << 3);
+  f32x4 oh[8], ol[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    oh[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ol[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nchunks) fetch(s);
+  for (int c = 0; c < nchunks; ++c) {
+    if (c + NST - 2 < nchunks)
+      wait_vmcnt<(NST - 2) * PER>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    if (c + NST - 1 < nchunks) fetch(c + NST - 1);
+    const uint16_t* sv = lds + (c % NST) * STAGE;
+    const uint16_t* spp = sv + VST;
+    u32x4 ph[2], pl[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const f32x4 x0 = __builtin_bit_cast(f32x4, lds_read16(spp, pcol[t][0]));
+      const f32x4 x1 = __builtin_bit_cast(f32x4, lds_read16(spp, pcol[t][1]));
+      const Split2 a = split2(x0[0], x0[1]), b = split2(x0[2], x0[3]);
+      const Split2 e = split2(x1[0], x1[1]), f = split2(x1[2], x1[3]);
+      ph[t] = u32x4{a.hi, b.hi, e.hi, f.hi};
+      pl[t] = u32x4{a.lo, b.lo, e.lo, f.lo};
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const u32x4 a = frag_read(sv, fo, t, i);
+        oh[i] = mfma<0, MFL_F16>(a, ph[t], oh[i]);
+        f32x4& corr = CHAINS == 2 ? ol[i] : oh[i];
+        corr = mfma<0, MFL_F16>(a, pl[t], corr);
+      }
+  }
+  // lane holds O_s^T dims 16 i + 4 g .. +3 of query qb*128 + wave*16 + lr
+  float* orow = Opart + ((int64_t)sp * nq + qb * kAttnQ + wave * 16 + lr) * kAttnD;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f32x4 o = oh[i];
+    if constexpr (CHAINS == 2) o = o + ol[i];
+    *reinterpret_cast<f32x4*>(orow + 16 * i + 4 * g) = o;
+  }
+}
+
+// Step 4: O[r][c..c+3] = (sum over slices s = 0, 1, ... of part[s][r][c..]) / l[r].
 __global__ __launch_bounds__(256) void reduce_slices(const float* __restrict__ part, int splits, int64_t stride,
-                                                   const float* __restrict__ l, float* __restrict__ O, int d,
-                                                   int64_t total) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  float acc = 0.f;
-  for (int s = 0; s < splits; ++s) acc += part[s * stride + i];
-  O[i] = acc / l[i / d];
+                                                   const float* __restrict__ l, float* __restrict__ O, int64_t total4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // f32x4 index
+  if (i >= total4) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < splits; ++s) acc += reinterpret_cast<const f32x4*>(part + s * stride)[i];
+  reinterpret_cast<f32x4*>(O)[i] = acc / l[i / (kAttnD / 4)];
 }
 
 struct Workspace {
-  int64_t s_off, m_off, l_off, part_off, total;
-  int splits;
+  int64_t s_off, m_off, l_off, part_off, k16_off, vt_off, total;
+  int kps, splits;
 };
 
 int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
-// Split count of the second GEMM: enough slices of K (multiples of 64 keys)
-// for about 512 workgroups over its (nq/128) output tiles.
-int choose_splits(int64_t nq, int64_t nk) {
-  const int64_t tiles = nq / 128;
-  int s = 1;
-  while (s < 32 && tiles * s < 512 && nk % (2 * s * 64) == 0) s *= 2;
-  return s;
+// Key slices of steps 1 and 3: about one workgroup per CU over the nq / 128
+// query blocks, whole 64-key chunks, the last slice possibly shorter.
+void choose_slices(int64_t nq, int64_t nk, int* kps, int* splits) {
+  const int64_t qblocks = nq / kAttnQ, chunks = nk / kAttnKV;
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>((256 + qblocks - 1) / qblocks, chunks));
+  const int64_t per = (chunks + want - 1) / want;
+  *kps = (int)(per * kAttnKV);
+  *splits = (int)((chunks + per - 1) / per);
 }
 
 Workspace plan(int64_t nq, int64_t nk, int64_t d) {
   Workspace w;
-  w.splits = choose_splits(nq, nk);
+  choose_slices(nq, nk, &w.kps, &w.splits);
   int64_t off = 0;
   w.s_off = off;
   off = align256(off + nq * nk * 4);
@@ -166,6 +435,10 @@ Workspace plan(int64_t nq, int64_t nk, int64_t d) {
   off = align256(off + nq * 4);
   w.part_off = off;
   off = align256(off + (int64_t)w.splits * nq * d * 4);
+  w.k16_off = off;
+  off = align256(off + nk * d * 2);
+  w.vt_off = off;
+  off = align256(off + nk * d * 2);
   w.total = off;
   return w;
 }
@@ -213,27 +486,33 @@ int attention_launch(int64_t nq, int64_t nk, int64_t d, const float* q, const fl
   float* m = (float*)(ws + w.m_off);
   float* l = (float*)(ws + w.l_off);
   float* part = (float*)(ws + w.part_off);
-  const int NQ = (int)nq, NK = (int)nk, D = (int)d;
+  uint16_t* k16 = (uint16_t*)(ws + w.k16_off);
+  uint16_t* vt = (uint16_t*)(ws + w.vt_off);
+  const int NQ = (int)nq, qblocks = (int)(nq / kAttnQ), nwg = qblocks * w.splits, xcd_map = nwg % 8 == 0;
   int st;
-  // 1. S = split(Q) . round(K)^T ; K (nk x d row-major) is B = K^T column-major.
-  st = dispatch_split_modes<MFL_F16, true, true>(true, false, chains, false, q, d, k, d, S, nk, NQ, NK, D, 1, D, 0, 0,
-                                                 s);
-  if (st != MFL_OK) return st;
+  hipLaunchKernelGGL(attn_prep_kvt, dim3((unsigned)(nk / kAttnKV)), dim3(256), 0, s, k, v, k16, vt, nk);
+  // 1. S = split(Q) . round(K)^T, chunk-blocked
+  if (chains == 2)
+    hipLaunchKernelGGL(attn_scores<2>, dim3(nwg), dim3(512), 0, s, q, k16, S, NQ, nk, w.kps, qblocks, xcd_map);
+  else
+    hipLaunchKernelGGL(attn_scores<1>, dim3(nwg), dim3(512), 0, s, q, k16, S, NQ, nk, w.kps, qblocks, xcd_map);
+  if ((st = launch_status()) != MFL_OK) return st;
   // 2. row softmax pieces, P~ in place.
   if (nk <= (int64_t)kSoftmaxThreads * kSoftmaxVec * 4)
-    hipLaunchKernelGGL(softmax_rows_regs, dim3(NQ), dim3(kSoftmaxThreads), 0, s, S, nk, NK, m, l);
+    hipLaunchKernelGGL(softmax_rows_regs, dim3(NQ), dim3(kSoftmaxThreads), 0, s, S, NQ, (int)nk, m, l);
   else
-    hipLaunchKernelGGL(softmax_rows_2pass, dim3(NQ), dim3(kSoftmaxThreads), 0, s, S, nk, NK, m, l);
+    hipLaunchKernelGGL(softmax_rows_2pass, dim3(NQ), dim3(kSoftmaxThreads), 0, s, S, NQ, nk, m, l);
   if ((st = launch_status()) != MFL_OK) return st;
-  // 3. partial O per K slice: split(P~) . round(V) ; V (nk x d row-major) is B row-major.
-  const int kps = NK / w.splits;
-  st = dispatch_split_modes<MFL_F16, true, false>(true, false, chains, false, S, nk, v, d, part, d, NQ, D, NK, w.splits,
-                                                  kps, nq * d, 0, s);
-  if (st != MFL_OK) return st;
+  // 3. partial O per key slice: split(P~) . round(V)
+  if (chains == 2)
+    hipLaunchKernelGGL(attn_pv<2>, dim3(nwg), dim3(512), 0, s, S, vt, part, NQ, nk, w.kps, qblocks, xcd_map);
+  else
+    hipLaunchKernelGGL(attn_pv<1>, dim3(nwg), dim3(512), 0, s, S, vt, part, NQ, nk, w.kps, qblocks, xcd_map);
+  if ((st = launch_status()) != MFL_OK) return st;
   // 4. fixed-order sum of the slices, then divide by l.
-  const int64_t total = nq * d;
-  hipLaunchKernelGGL(reduce_slices, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, w.splits, nq * d, l,
-                     o, D, total);
+  const int64_t total4 = nq * d / 4;
+  hipLaunchKernelGGL(reduce_slices, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0, s, part, w.splits, nq * d, l,
+                     o, total4);
   return launch_status();
 }
 

@@ -6,18 +6,6 @@
 namespace mfl {
 namespace attn_detail {
 
-// Packed hi/lo split of two fp32 values into fp16 pairs: hi = RNE16(x),
-// lo = RNE16(x - hi), with x - hi exact in fp32.
-struct Split2 {
-  uint32_t hi, lo;
-};
-__device__ __forceinline__ Split2 split2(float a, float b) {
-  const h16x2 h = __builtin_convertvector(f32x2{a, b}, h16x2);
-  const f32x2 hf = __builtin_convertvector(h, f32x2);
-  const h16x2 l = __builtin_convertvector(f32x2{a - hf.x, b - hf.y}, h16x2);
-  return {__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};
-}
-
 // The same split with x - hi taken by v_fma_mix_f32 straight from the fp16 hi
 // (x * 1 - hi in one instruction; the difference is exact, so the result is the
 // same as converting hi back and subtracting: checked on the device for every
@@ -88,16 +76,6 @@ __device__ __forceinline__ float swap_max(float x, bool by32) {
   return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
 __device__ __forceinline__ float max_over_lane_groups(float x) { return swap_max(swap_max(x, false), true); }
-
-// Workgroup -> (query block, key slice).  With xcd_map the workgroups that an
-// XCD receives (hardware dispatch sends workgroup b to XCD b mod 8) cover a
-// contiguous range of key slices for every query block, so each XCD's L2 holds
-// only its own slices of K16 / V16^T.
-__device__ __forceinline__ void attn_block_of(int b, int nwg, int qblocks, int xcd_map, int& qb, int& sp) {
-  const int i = xcd_map ? (b & 7) * (nwg >> 3) + (b >> 3) : b;
-  qb = i % qblocks;
-  sp = i / qblocks;
-}
 
 // One workgroup: 128 queries (8 waves of 16) x one slice of keys_per_split keys.
 // Scores are kept in base-2 units (Q is scaled by log2 e before its split), so

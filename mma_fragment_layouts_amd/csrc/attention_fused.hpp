@@ -42,6 +42,28 @@ constexpr float kAttnSlack = 8.f;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 
+// Packed hi/lo split of two fp32 values into fp16 pairs: hi = RNE16(x),
+// lo = RNE16(x - hi), with x - hi exact in fp32.
+struct Split2 {
+  uint32_t hi, lo;
+};
+__device__ __forceinline__ Split2 split2(float a, float b) {
+  const h16x2 h = __builtin_convertvector(f32x2{a, b}, h16x2);
+  const f32x2 hf = __builtin_convertvector(h, f32x2);
+  const h16x2 l = __builtin_convertvector(f32x2{a - hf.x, b - hf.y}, h16x2);
+  return {__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l)};
+}
+
+// Workgroup -> (query block, key slice).  With xcd_map the workgroups that an
+// XCD receives (hardware dispatch sends workgroup b to XCD b mod 8) cover a
+// contiguous range of key slices for every query block, so each XCD's L2 holds
+// only its own slices of K16 / V16^T.
+__device__ __forceinline__ void attn_block_of(int b, int nwg, int qblocks, int xcd_map, int& qb, int& sp) {
+  const int i = xcd_map ? (b & 7) * (nwg >> 3) + (b >> 3) : b;
+  qb = i % qblocks;
+  sp = i / qblocks;
+}
+
 // K row of key r (0..31) inside its 32-key block of the k-major V16 tile.
 MFL_HD constexpr int vt_key_pos(int r) { return 8 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3); }
 

@@ -370,6 +370,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier after this wave's LDS operations have completed.  Unlike
+// __syncthreads it does not wait for outstanding vector-memory loads (its
+// release fence would), so loads issued for later stages stay in flight; a
+// stage's direct-to-LDS loads are waited for with wait_vmcnt before it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Direct-to-LDS loads of one operand's R x 64 slab per stage.
 //   K-contiguous (A row-major, B column-major): R rows of 64 K values, 128 bytes
 //     each, chunk XOR swz<64>(row); a load instruction fills 8 rows.
