@@ -158,7 +158,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
       wait_vmcnt<(STAGES - 2) * LOADS>();
     else
       wait_vmcnt<0>();
-    __syncthreads();
+    // Beyond two stages the barrier must leave the later stages' loads in
+    // flight, which __syncthreads (its fence waits for every load) would not.
+    if constexpr (STAGES > 2)
+      lds_barrier();
+    else
+      __syncthreads();
     if constexpr (!LATE) {
       if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
       const int cur = (kt % STAGES) * STAGE;
@@ -289,9 +294,16 @@ static int dispatch_fast(int shape, const void* a, int64_t lda, const void* b, i
   if (count(256) >= 128)
     return s32 ? launch_fast<256, 256, 4, 4, 1, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)
                : launch_fast<256, 256, 4, 4, 0, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
-  if (count(128) >= 128 || AKM || BKM)
-    return s32 ? launch_fast<128, 128, 2, 2, 1, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s)
-               : launch_fast<128, 128, 2, 2, 0, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  // 128 x 128 tiles.  At most one per CU: 16 waves of 32 x 32 and three LDS
+  // stages (2048^3 20.5 us against 24.4 us with 4 waves of 64 x 64 and two
+  // stages; 1536^3 14.5 against 18.1).  More tiles: 4 waves and two stages, so
+  // that two workgroups share a CU (2560^3 35.7 us against 43.1).
+  if (count(128) >= 128 || AKM || BKM) {
+    if (s32) return launch_fast<128, 128, 2, 2, 1, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+    if (count(128) <= 256)
+      return launch_fast<128, 128, 4, 4, 0, DT, AKM, BKM, 3>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+    return launch_fast<128, 128, 2, 2, 0, DT, AKM, BKM>(a, lda, b, ldb, c, ldc, M, N, K, accumulate, s);
+  }
   // Small problems: 64 x 64 tiles with 4 waves of 32 x 32, or, with the
   // 16x16x32 instruction, 32 x 32 tiles (4 waves of 16 x 16) when 64-tiles
   // would give fewer than 128 workgroups.  Measured (bf16, kernel time): 1024^3
