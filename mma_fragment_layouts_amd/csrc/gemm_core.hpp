@@ -9,6 +9,7 @@
 // registers across the K loop and is materialised once.  These templates are
 // that design for CDNA4 wavefronts of 64 lanes.
 #pragma once
+#include <utility>
 #include "common.hpp"
 
 namespace mfl {
@@ -195,6 +196,42 @@ __device__ __forceinline__ u32x4 frag_read(const uint16_t* s, const KmFrag<SHAPE
   return lds_read_tr(s, o.off + kmaj_step<SHAPE>(kk, 0, f), kmaj_step<SHAPE>(0, 1, 0));
 }
 
+// ---- transpose reads the compiler does not see --------------------------------
+// The compiler makes every ds_read_b64_tr_b16 that follows a direct-to-LDS load
+// wait for that load (s_waitcnt vmcnt(0)): it cannot tell the two buffers apart.
+// With a ring of stages that wait drains every prefetch at each K step.  The
+// same reads issued as inline assembly are invisible to its load tracking, so
+// the kernel waits for them itself (s_waitcnt lgkmcnt(0)) and then passes each
+// fragment through an empty asm that the MFMAs depend on, so no MFMA is moved
+// above the wait.  The stage a read uses is never a load's target before the
+// next workgroup barrier, which waits for all LDS operations.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+__device__ __forceinline__ uint32_t lds_address(const uint16_t* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr_asm(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "immediate LDS offset");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF) : "memory");
+  return r;
+}
+// Fragment F of MFMA K step KK from a k-major tile; base is the LDS byte
+// address of the lane's base element (tile + KmFrag::off).
+template <int SHAPE, int KK, int F>
+__device__ __forceinline__ u32x4 frag_read_tr_asm(uint32_t base) {
+  const u32x2 lo = lds_read_tr_asm<2 * kmaj_step<SHAPE>(KK, 0, F)>(base);
+  const u32x2 hi = lds_read_tr_asm<2 * kmaj_step<SHAPE>(KK, 1, F)>(base);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
 // One BK-deep slab of the wave's TM x TN grid of MFMA tiles: for each MFMA K
 // step, read the A and B fragments from LDS and accumulate into registers.
 // MASKK: when kvalid < BK only the first kvalid (a multiple of 8) K positions of
@@ -225,6 +262,57 @@ __device__ __forceinline__ void mma_slab(const uint16_t* sA, const uint16_t* sB,
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma<SHAPE, DT>(a[i], b[j], acc[i][j]);
   }
+}
+
+// mma_slab for slabs with a k-major operand (AKM: A, BKM: B), its fragments
+// read by frag_read_tr_asm; the other operand's by the ordinary 16-byte reads.
+template <int SHAPE, int DT, int TM, int TN, int BK, bool AKM, bool BKM, bool MASKK, class RA, class RB>
+__device__ __forceinline__ void mma_slab_tr_asm(const uint16_t* sA, const uint16_t* sB, const RA& fa, const RB& fb,
+                                                typename Shape<SHAPE>::Acc (&acc)[TM][TN], int kvalid) {
+  static_assert(AKM || BKM, "a k-major operand");
+  constexpr int MN = Shape<SHAPE>::MN, KM = Shape<SHAPE>::K;
+  uint32_t baseA = 0, baseB = 0;
+  if constexpr (AKM) baseA = lds_address(sA + fa.off);
+  if constexpr (BKM) baseB = lds_address(sB + fb.off);
+  static_for<BK / KM>([&](auto kkc) {
+    constexpr int kk = decltype(kkc)::value;
+    u32x4 a[TM], b[TN];
+    static_for<TM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (AKM)
+        a[i] = frag_read_tr_asm<SHAPE, kk, i>(baseA);
+      else
+        a[i] = frag_read(sA, fa, kk, i);
+    });
+    static_for<TN>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (BKM)
+        b[j] = frag_read_tr_asm<SHAPE, kk, j>(baseB);
+      else
+        b[j] = frag_read(sB, fb, kk, j);
+    });
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if constexpr (AKM) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) asm volatile("" : "+v"(a[i]));
+    }
+    if constexpr (BKM) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(b[j]));
+    }
+    if constexpr (MASKK) {
+      if (kvalid < BK && kk * KM + 8 * ((int)(threadIdx.x & 63) / MN) >= kvalid) {  // kvalid is wave-uniform
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[j] = u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma<SHAPE, DT>(a[i], b[j], acc[i][j]);
+  });
 }
 
 // mma_slab with part of the slab's last MFMA K step carried over the next

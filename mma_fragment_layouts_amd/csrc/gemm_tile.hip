@@ -148,6 +148,11 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
   // the barrier would hold up the step's first reads for their whole latency.
   // Issued there, they still have most of the step to land.
   constexpr bool LATE = AKM || BKM;
+  // With more than two stages the k-major fragments are read by transpose reads
+  // the compiler does not track (mma_slab_tr_asm), so the next stage is issued
+  // right after the barrier and stays in flight through the step: 2048^3 with
+  // 128 x 128 tiles, k-major A and/or B, 22.3-23.2 us against 30.3-32.6 us.
+  constexpr bool TRASM = (AKM || BKM) && STAGES > 2 && CARRY == 0;
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
     if (st < KT) issue(st, st * BK);
@@ -164,7 +169,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_fast_kernel(const uint16_t
       lds_barrier();
     else
       __syncthreads();
-    if constexpr (!LATE) {
+    if constexpr (TRASM) {
+      if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
+      const int cur = (kt % STAGES) * STAGE;
+      mma_slab_tr_asm<SHAPE, DT, TM, TN, BK, AKM, BKM, EDGE>(lds + cur, lds + cur + BM * BK, fa, fb, acc,
+                                                             K - kt * BK);
+    } else if constexpr (!LATE) {
       if (kt + STAGES - 1 < KT) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
       const int cur = (kt % STAGES) * STAGE;
       if constexpr (CARRY > 0)
