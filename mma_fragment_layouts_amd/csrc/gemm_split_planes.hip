@@ -80,23 +80,90 @@ __global__ __launch_bounds__(kPlanesWGM* kPlanesWGN * 64) void gemm_split_planes
   for (int ch = 0; ch < P::CHAINS; ++ch) zero_acc<SHAPE, TM, TN>(acc[ch]);
 
   const int KT = (K + BK - 1) / BK;  // a multiple of BK unless EDGE
-  // With a k-major plane the next stage is requested after the fragment reads
-  // of this stage's first MFMA K step: the compiler makes an LDS transpose
-  // read that follows a direct-to-LDS load wait for it (it cannot tell the
-  // buffers apart), which would hold up the step's first reads for the whole
-  // load latency.
-  constexpr bool LATE = AKM || BKM;
+  // A k-major plane's fragments are read by transpose reads the compiler does
+  // not track (frag_read_tr_asm): a tracked one would wait for the next
+  // stage's loads, issued right after the barrier, to land.  4096^3, 3
+  // chains, A column-major and B row-major, same box: 416-417 us per call
+  // against 438-441 us with tracked reads and the loads issued after each
+  // step's first reads (K-contiguous planes 381-383 us).
+  constexpr bool TRASM = AKM || BKM;
   constexpr int KS = BK / Shape<SHAPE>::K;
+  // One slab with k-major plane(s): every fragment of a K step read, waited
+  // for, then the step's MFMAs (same products and order as below).
+  auto slab_tr = [&](const uint16_t* st, int kvalid) {
+    uint32_t ba = 0, bb = 0;
+    if constexpr (AKM) ba = lds_address(st + fa.off);
+    if constexpr (BKM) bb = lds_address(st + 2 * PLANE + fb.off);
+    static_for<KS>([&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      u32x4 ah[TM], al[TM], bh[TN], bl[TN];
+      static_for<TM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (AKM) {
+          ah[i] = frag_read_tr_asm<SHAPE, kk, i>(ba);
+          al[i] = frag_read_tr_asm<SHAPE, kk, i>(ba + 2 * PLANE);
+        } else {
+          ah[i] = frag_read(st, fa, kk, i);
+          al[i] = frag_read(st + PLANE, fa, kk, i);
+        }
+      });
+      static_for<TN>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (BKM) {
+          bh[j] = frag_read_tr_asm<SHAPE, kk, j>(bb);
+          bl[j] = frag_read_tr_asm<SHAPE, kk, j>(bb + 2 * PLANE);
+        } else {
+          bh[j] = frag_read(st + 2 * PLANE, fb, kk, j);
+          bl[j] = frag_read(st + 3 * PLANE, fb, kk, j);
+        }
+      });
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if constexpr (AKM) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          asm volatile("" : "+v"(ah[i]));
+          asm volatile("" : "+v"(al[i]));
+        }
+      }
+      if constexpr (BKM) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          asm volatile("" : "+v"(bh[j]));
+          asm volatile("" : "+v"(bl[j]));
+        }
+      }
+      if constexpr (EDGE) {
+        if (kvalid < BK && kk * Shape<SHAPE>::K + 8 * (lane / MN) >= kvalid) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) ah[i] = al[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bh[j] = bl[j] = u32x4{0, 0, 0, 0};
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < P::NPROD; ++p)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const u32x4 av = P::a_lo(p) ? al[i] : ah[i];
+            const u32x4 bv = P::b_lo(p) ? bl[j] : bh[j];
+            acc[P::chain(p)][i][j] = mfma<SHAPE, DT>(av, bv, acc[P::chain(p)][i][j]);
+          }
+    });
+  };
   if (KT > 0) issue(0, 0);
   for (int kt = 0; kt < KT; ++kt) {
     // this wave's loads of stage kt have landed; after the barrier every
     // wave's have, and stage kt-1 (the buffer refilled next) is retired
     wait_vmcnt<0>();
     __syncthreads();
-    if constexpr (!LATE) {
-      if (kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * BK);
-    }
+    if (kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * BK);
     const uint16_t* st = lds + (kt & 1) * STAGE;
+    if constexpr (TRASM) {
+      slab_tr(st, K - kt * BK);
+      continue;
+    }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       u32x4 ah[TM], al[TM], bh[TN], bl[TN];
@@ -109,9 +176,6 @@ __global__ __launch_bounds__(kPlanesWGM* kPlanesWGN * 64) void gemm_split_planes
       for (int j = 0; j < TN; ++j) {
         bh[j] = frag_read(st + 2 * PLANE, fb, kk, j);
         bl[j] = frag_read(st + 3 * PLANE, fb, kk, j);
-      }
-      if constexpr (LATE) {
-        if (kk == 0 && kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * BK);
       }
       if constexpr (EDGE) {
         // K positions 8*(lane/16) .. +7 of MFMA step kk (the operand numeral);
