@@ -41,6 +41,19 @@ def test_attention_small(nq, nk, chains, algo):
     assert err <= 5e-6
 
 
+@pytest.mark.parametrize("chains", [1, 2])
+def test_attention_materialised_uneven_slices(chains):
+    """128 queries x 32,896 keys: 514 chunks of 64 keys, so the materialised
+    path's key slices hold 3 chunks each and the last one a single chunk.
+    Every row against the oracle."""
+    q, k, v = inputs.attention(128, 514 * 64)
+    say("attention uneven slices", chains)
+    o = run_attention(q, k, v, chains, mfl.ATTN_MATERIALISED)
+    err = R.rel_error(o, R.attention_ref(q, k, v))
+    print(f"attention 128x{514 * 64} chains={chains} materialised err={err:.3e}")
+    assert err <= 5e-6
+
+
 @pytest.mark.parametrize("algo", ALGOS)
 def test_attention_uniform_closed_form(algo):
     """Q = 0: every score is 0, P is uniform and O is the column mean of Q16(V)."""
