@@ -108,11 +108,16 @@ struct SplitLoader {
           lds_write16(lo, lds_chunk<BK>(r, c), v);
         }
       } else {
+        // k-major tile (the kmaj_chunk layout of the 16x16x32 instruction, as
+        // the direct-to-LDS k-major slabs): the 8 rows rc*8 .. +7 at K row k
+        // are one 16-byte chunk
         const int k = idx / (R / 8), rc = idx % (R / 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          hi[lds_elem<BK>(rc * 8 + e, k)] = h[e];
-          if constexpr (SPLIT) lo[lds_elem<BK>(rc * 8 + e, k)] = l[e];
+        u32x4 v;
+        __builtin_memcpy(&v, h, 16);
+        lds_write16(hi, lds_elemKM<0>(k, rc * 8), v);
+        if constexpr (SPLIT) {
+          __builtin_memcpy(&v, l, 16);
+          lds_write16(lo, lds_elemKM<0>(k, rc * 8), v);
         }
       }
     }
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_split_kernel(const float* 
   constexpr int STAGE = TA * (P::SA ? 2 : 1) + TB * (P::SB ? 2 : 1);
   using Acc = typename Shape<SHAPE>::Acc;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
 
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, &tm, &tn);
@@ -156,7 +161,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_split_kernel(const float* 
   auto b_hi = [&](int s) { return lds + s * STAGE + TA * (P::SA ? 2 : 1); };
   auto b_lo = [&](int s) { return lds + s * STAGE + TA * (P::SA ? 2 : 1) + TB; };
 
-  const FragOffsets<SHAPE, BK> fa(wr0, lane), fb(wc0, lane);
+  // K-contiguous operands: swizzled row tiles read 16 bytes at a time;
+  // K-strided ones: k-major tiles read with the transpose read.
+  using RA = std::conditional_t<AK, FragOffsets<SHAPE, BK>, KmFrag<SHAPE, BM, WM, TM>>;
+  using RB = std::conditional_t<BKC, FragOffsets<SHAPE, BK>, KmFrag<SHAPE, BN, WN, TN>>;
+  const RA fa(wr0, lane);
+  const RB fb(wc0, lane);
   Acc acc[P::CHAINS][TM][TN];
 #pragma unroll
   for (int ch = 0; ch < P::CHAINS; ++ch) zero_acc<SHAPE, TM, TN>(acc[ch]);
@@ -182,13 +192,13 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_split_kernel(const float* 
         u32x4 ah[TM], al[TM], bh[TN], bl[TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          ah[i] = lds_read16(a_hi(cur), fa.off[kk] + i * MN * BK);
-          if constexpr (P::SA) al[i] = lds_read16(a_lo(cur), fa.off[kk] + i * MN * BK);
+          ah[i] = frag_read(a_hi(cur), fa, kk, i);
+          if constexpr (P::SA) al[i] = frag_read(a_lo(cur), fa, kk, i);
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          bh[j] = lds_read16(b_hi(cur), fb.off[kk] + j * MN * BK);
-          if constexpr (P::SB) bl[j] = lds_read16(b_lo(cur), fb.off[kk] + j * MN * BK);
+          bh[j] = frag_read(b_hi(cur), fb, kk, j);
+          if constexpr (P::SB) bl[j] = frag_read(b_lo(cur), fb, kk, j);
         }
         // Product-major order: between two products on one accumulator there
         // are TM*TN independent MFMAs, and within one accumulator the K step's
