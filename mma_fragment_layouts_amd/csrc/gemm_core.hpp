@@ -20,7 +20,9 @@ namespace mfl {
 //               (row-major A or column-major B: K contiguous); 16-byte loads
 //               along K, 16-byte LDS writes.
 //   KC = false: element (r, k) is at base[(k0 + k)*ld + r0 + r] (K strided);
-//               16-byte loads along R, scattered 2-byte LDS writes.
+//               16-byte loads along R, 16-byte LDS writes into a k-major tile
+//               (the kmaj_chunk layout of the 16x16x32 instruction, read with
+//               the transpose read).
 // EDGE enables masking: K positions >= k_total are zero (in both operands, so a
 // NaN in padding never meets a zero), R positions past rows_total are zero (KC =
 // false) or repeat the last row (KC = true) and are never stored by the
@@ -72,11 +74,9 @@ struct TileLoader {
         const int r = idx / (BK / 8), c = idx % (BK / 8);
         lds_write16(lds, lds_chunk<BK>(r, c), reg[i]);
       } else {
+        static_assert(BK == 64 && (R == 128 || R == 256), "k-major tile shape");
         const int k = idx / (R / 8), rc = idx % (R / 8);
-        uint16_t h[8];
-        __builtin_memcpy(h, &reg[i], 16);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lds[lds_elem<BK>(rc * 8 + e, k)] = h[e];
+        lds_write16(lds, lds_elemKM<0>(k, rc * 8), reg[i]);
       }
     }
   }

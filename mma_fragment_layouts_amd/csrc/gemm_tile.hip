@@ -29,7 +29,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_tile_kernel(const uint16_t
   constexpr int STAGE = (BM + BN) * BK;
   using Acc = typename Shape<SHAPE>::Acc;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
 
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, &tm, &tn);
@@ -37,7 +37,13 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_tile_kernel(const uint16_t
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr0 = (wave / WGN) * WM, wc0 = (wave % WGN) * WN;
-  const FragOffsets<SHAPE, BK> fa(wr0, lane), fb(wc0, lane);
+  // K-strided operands are staged k-major (TileLoader) and read with the
+  // transpose read; the k-major layout is that of the 16x16x32 instruction.
+  static_assert(SHAPE == 0 || (AK && BKC), "k-major tiles take the 16x16x32 instruction");
+  using RA = std::conditional_t<AK, FragOffsets<SHAPE, BK>, KmFrag<SHAPE, BM, WM, TM>>;
+  using RB = std::conditional_t<BKC, FragOffsets<SHAPE, BK>, KmFrag<SHAPE, BN, WN, TN>>;
+  const RA fa(wr0, lane);
+  const RB fb(wc0, lane);
 
   Acc acc[TM][TN];
   zero_acc<SHAPE, TM, TN>(acc);
