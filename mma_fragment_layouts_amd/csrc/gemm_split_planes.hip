@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kPlanesWGM* kPlanesWGN * 64) void gemm_split_planes
   // A k-major plane's fragments are read by transpose reads the compiler does
   // not track (frag_read_tr_asm): a tracked one would wait for the next
   // stage's loads, issued right after the barrier, to land.  4096^3, 3
-  // chains, A column-major and B row-major, same box: 416-417 us per call
+  // chains, A column-major and B row-major, one machine: 416-417 us per call
   // against 438-441 us with tracked reads and the loads issued after each
   // step's first reads (K-contiguous planes 381-383 us).
   constexpr bool TRASM = AKM || BKM;
