@@ -70,38 +70,39 @@ __device__ __forceinline__ float block_reduce(float x, float* red) {
 }
 
 // K16 = RNE16(K), key-major like K; V16T = RNE16(V) transposed, V16T[d][key].
-// One workgroup per 64 keys: each thread rounds 32 consecutive values of the
-// K block, and one pair of keys x 16 dims of the V block, whose halves it
-// packs per dim into 32-bit words of an LDS tile (a dim row of 32 key pairs,
-// padded to 33 words); the tile leaves as 128-byte rows of V16T.
-__global__ __launch_bounds__(256) void attn_prep_kvt(const float* __restrict__ K, const float* __restrict__ V,
+// One workgroup of 512 threads per 64 keys: each thread rounds 16 consecutive
+// values of the K block, and one pair of keys x 8 dims of the V block, whose
+// halves it packs per dim into 32-bit words of an LDS tile (a dim row of 32
+// key pairs, padded to 33 words); the tile leaves as 128-byte rows of V16T,
+// four threads per row.
+__global__ __launch_bounds__(512) void attn_prep_kvt(const float* __restrict__ K, const float* __restrict__ V,
                                                     uint16_t* __restrict__ Kq, uint16_t* __restrict__ VqT, int64_t nk) {
   constexpr int PADW = 33;
   __shared__ uint32_t t[kAttnD * PADW];
   const int64_t key0 = (int64_t)blockIdx.x * kAttnKV;
   const int tid = threadIdx.x;
   {
-    const int64_t base = key0 * kAttnD + tid * 32;
-    uint32_t w[16];
+    const int64_t base = key0 * kAttnD + tid * 16;
+    uint32_t w[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(K + base + 4 * q);
       const Split2 a = split2(x[0], x[1]), b = split2(x[2], x[3]);
       w[2 * q] = a.hi;
       w[2 * q + 1] = b.hi;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       u32x4 o;
       __builtin_memcpy(&o, w + 4 * q, 16);
       *reinterpret_cast<u32x4*>(Kq + base + 8 * q) = o;
     }
   }
   {
-    const int kp = tid >> 3, d0 = (tid & 7) * 16;
+    const int kp = tid >> 4, d0 = (tid & 15) * 8;
     const float* r0 = V + (key0 + 2 * kp) * kAttnD + d0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       const f32x4 a = *reinterpret_cast<const f32x4*>(r0 + 4 * q);
       const f32x4 b = *reinterpret_cast<const f32x4*>(r0 + kAttnD + 4 * q);
 #pragma unroll
@@ -109,11 +110,11 @@ __global__ __launch_bounds__(256) void attn_prep_kvt(const float* __restrict__ K
     }
   }
   __syncthreads();
-  const int d = tid >> 1, h = tid & 1;
+  const int d = tid >> 2, h = tid & 3;  // dim row d, keys 16 h .. +15
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t* r = t + d * PADW + 16 * h + 4 * q;
-    *reinterpret_cast<u32x4*>(VqT + d * nk + key0 + 32 * h + 8 * q) = u32x4{r[0], r[1], r[2], r[3]};
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t* r = t + d * PADW + 8 * h + 4 * q;
+    *reinterpret_cast<u32x4*>(VqT + d * nk + key0 + 16 * h + 8 * q) = u32x4{r[0], r[1], r[2], r[3]};
   }
 }
 
@@ -490,7 +491,7 @@ int attention_launch(int64_t nq, int64_t nk, int64_t d, const float* q, const fl
   uint16_t* vt = (uint16_t*)(ws + w.vt_off);
   const int NQ = (int)nq, qblocks = (int)(nq / kAttnQ), nwg = qblocks * w.splits, xcd_map = nwg % 8 == 0;
   int st;
-  hipLaunchKernelGGL(attn_prep_kvt, dim3((unsigned)(nk / kAttnKV)), dim3(256), 0, s, k, v, k16, vt, nk);
+  hipLaunchKernelGGL(attn_prep_kvt, dim3((unsigned)(nk / kAttnKV)), dim3(512), 0, s, k, v, k16, vt, nk);
   // 1. S = split(Q) . round(K)^T, chunk-blocked
   if (chains == 2)
     hipLaunchKernelGGL(attn_scores<2>, dim3(nwg), dim3(512), 0, s, q, k16, S, NQ, nk, w.kps, qblocks, xcd_map);
