@@ -85,7 +85,7 @@ def test_wrong_declared_order_gives_a_different_product():
 
 @pytest.mark.parametrize("mnk", [(200, 136, 100), (129, 257, 72), (1, 1, 1), (17, 300, 8), (384, 384, 1000),
                                  (256, 512, 130)])
-@pytest.mark.parametrize("orders", [(0, 1), (1, 0)])
+@pytest.mark.parametrize("orders", [(0, 1), (1, 0), (0, 0), (1, 1)])
 def test_ragged_sizes(mnk, orders):
     m, n, k = mnk
     rng = np.random.default_rng(m * 7 + n * 3 + k)
