@@ -62,7 +62,6 @@ __device__ __forceinline__ float from16(uint16_t h) {
   else
     return (float)__builtin_bit_cast(f16, h);
 }
-__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
 // ---- swizzled LDS tile -----------------------------------------------------
 // A tile of R rows (M or N index) by BK K-values of 16-bit data, K contiguous,
@@ -102,10 +101,6 @@ static_assert(swz_period16<64>() && swz_period16<32>(), "LDS swizzle must depend
 template <int BK>
 __device__ __forceinline__ int lds_chunk(int row, int chunk) {
   return row * BK + ((chunk ^ swz<BK>(row)) << 3);
-}
-template <int BK>
-__device__ __forceinline__ int lds_elem(int row, int k) {
-  return lds_chunk<BK>(row, k >> 3) + (k & 7);
 }
 
 // ---- k-major LDS tiles and the CDNA4 transpose read ---------------------------
