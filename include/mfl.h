@@ -358,6 +358,8 @@ MFL_API int attention_split_fp32(int64_t nq, int64_t nk, int64_t d, const float 
  * static device array of MFL_ATTN_STATIC_SCRATCH_BYTES that the library holds
  * on every GPU it runs on until the process ends; the first call on a device
  * looks up that device's copy (hipGetSymbolAddress), later calls reuse it.
+ * The copy used is the current device's (hipGetDevice at the call), so the
+ * stream and every pointer must belong to that device.
  * Calls whose attention_workspace_bytes exceeds the array return MFL_ESCRATCH
  * before any device work: 64 MiB holds algo 1 (32.3 MiB) and algo 2 (48.3 MiB)
  * at 2048 queries x 32768 keys, while algo 0, which materialises the nq x nk
