@@ -332,9 +332,11 @@ MFL_API int attention_workspace_bytes(int64_t nq, int64_t nk, int64_t d, int alg
  *   O = (P~ V) / l with P~ split into f16 hi/lo and V rounded once to f16.
  * `chains` (1 or 2) selects single-chain or separate hi/lo accumulators for
  * both products.  No causal mask and no 1/sqrt(d) scaling are applied.
- *   algo 0: the four steps as separate kernels, S and P~ materialised in the
- *           workspace (scores per 128 queries and key slice, row softmax,
- *           P~ V per key slice, fixed-order reduce of the slices);
+ *   algo 0: S materialised in the workspace: scores per 128 queries and key
+ *           slice, which also keep each slice's row maxima; P~ V per key
+ *           slice, forming P~ from S and the row maximum as it is loaded and
+ *           summing it per row; a fixed-order reduce of the slices' partial O
+ *           and row sums;
  *   algo 1: fused — per 128 queries and key slice, both products and an online
  *           softmax (running max, rescaled accumulators) stay in registers and
  *           LDS; key slices are merged by their exp(m_s - m) weights;

@@ -4,23 +4,29 @@
 // FP16 hi and lo half; "The fix": hi and lo products in separate accumulators).
 //
 //   1. S = Q K^T           Q split into f16 hi/lo, K rounded once
-//   2. m = rowmax S, P~ = exp(S - m), l = rowsum P~          (fp32, in place)
+//   2. m = rowmax S, P~ = exp(S - m), l = rowsum P~           (fp32)
 //   3. O_s = P~[:, slice s] V[slice s, :]   per key slice, P~ split, V rounded once
 //   4. O = (sum_s O_s) / l  slices summed in a fixed order
+//
+// Step 2 has no kernel of its own.  The scores kernel keeps each key slice's
+// row maxima as it stores S; the P~ V kernel takes m as the maximum of those,
+// forms every P~ entry from S and m as it loads S (so P~ is never stored), and
+// adds the entries it forms into the slice's row sum; the reduce adds the
+// slices' sums into l.
 //
 // Normalisation is deferred to step 4: P~ lies in (0, 1] with its maximum
 // exactly 1, whereas the normalised probabilities (about 1/nk) would fall in
 // fp16's subnormal range and lose most of their lo half.  softmax(S) V equals
-// (P~ V) / l exactly in real arithmetic.  This version materialises S / P~ in
-// the caller's workspace (HBM-bound); it keeps every step on the device.
+// (P~ V) / l exactly in real arithmetic.  This version materialises S in the
+// caller's workspace (HBM-bound); it keeps every step on the device.
 //
 // Kernels: attn_prep_kvt rounds K into K16 (key-major) and V into V16T (one
 // row of nk keys per dim); attn_scores computes S for 128 queries and one key
 // slice, Q's hi/lo halves held in registers and K16 chunks of 64 keys streamed
-// through LDS; the row softmax reads each row once and rewrites it; attn_pv
-// streams P~ and V16T chunks through LDS.  S and P~ are stored chunk-blocked,
-// S[key / 64][q][key % 64]: the 128 queries x 64 keys a workgroup handles per
-// chunk are 32 KiB of contiguous memory, written and read whole.
+// through LDS; attn_pv streams S and V16T chunks through LDS; reduce_slices
+// sums the slices.  S is stored chunk-blocked, S[key / 64][q][key % 64]: the
+// 128 queries x 64 keys a workgroup handles per chunk are 32 KiB of contiguous
+// memory, written and read whole.
 #include <algorithm>
 #include <mutex>
 
@@ -34,40 +40,11 @@ int launch_attn_fused(int64_t nq, int64_t nk, const float* q, const float* k, co
 
 namespace {
 
-constexpr int kSoftmaxThreads = 512;
-constexpr int kSoftmaxVec = 16;  // f32x4 per thread: rows up to 32768 stay in registers
 // P~ = exp(s - m) is taken as 2^((s - m) log2 e) with the hardware exp2.
 constexpr float kLog2e = 1.4426950408889634f;
-
-// Element (q, key) of the chunk-blocked nq x nk layout.
-__device__ __forceinline__ int64_t blk_index(int64_t nq, int q, int64_t key) {
-  return ((key >> 6) * nq + q) * kAttnKV + (key & 63);
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
-// Block-wide reduction of one value per thread (kSoftmaxThreads threads).
-template <bool MAX>
-__device__ __forceinline__ float block_reduce(float x, float* red) {
-  x = MAX ? wave_max(x) : wave_sum(x);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = x;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int i = 1; i < kSoftmaxThreads / 64; ++i) r = MAX ? fmaxf(r, red[i]) : r + red[i];
-  return r;
-}
+// One entry of P~ from its score and the row maximum.  The P~ V kernel forms
+// each entry once and both feeds it to the MFMAs and adds it to the row sum l.
+__device__ __forceinline__ float p_tilde(float s, float m) { return __builtin_amdgcn_exp2f((s - m) * kLog2e); }
 
 // K16 = RNE16(K), key-major like K; V16T = RNE16(V) transposed, V16T[d][key].
 // One workgroup of 512 threads per 64 keys: each thread rounds 16 consecutive
@@ -129,12 +106,14 @@ __device__ __forceinline__ int slice_chunks(int sp, int kps, int64_t nk) {
 // Each wave holds the B fragments of its 16 queries' hi and lo halves for the
 // whole slice; per 64-key chunk it computes S^T (64 keys x 16 queries) =
 // K16 . Q^T with the hi products in one chain and the lo products in a second
-// (CHAINS == 2) or the same one, adds the chains in fp32 and stores the tile.
-// K16 chunks arrive by direct-to-LDS loads, two stages.
+// (CHAINS == 2) or the same one, adds the chains in fp32, stores the tile and
+// keeps the running maximum of its queries' scores, written per query and
+// slice at the end (Ms[slice][q]).  K16 chunks arrive by direct-to-LDS loads,
+// two stages.
 template <int CHAINS>
 __global__ __launch_bounds__(512) void attn_scores(const float* __restrict__ Q, const uint16_t* __restrict__ Kq,
-                                                   float* __restrict__ S, int nq, int64_t nk, int kps, int qblocks,
-                                                   int xcd_map) {
+                                                   float* __restrict__ S, float* __restrict__ Ms, int nq, int64_t nk,
+                                                   int kps, int qblocks, int xcd_map) {
   constexpr int BK = 64, KT = kAttnKV * BK, STAGE = 2 * KT, NW = 8, LOADS = 2;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
   int qb, sp;
@@ -184,6 +163,7 @@ __global__ __launch_bounds__(512) void attn_scores(const float* __restrict__ Q, 
   // lane's keys 16 kt + 4 g .. +3 of each chunk, query qw + lr
   float* srow = S + ((kbeg >> 6) * nq + qw + lr) * kAttnKV + 4 * g;
   const int64_t cstride = (int64_t)nq * kAttnKV;
+  float mrun = -INFINITY;  // maximum of the lane's scores of query qw + lr
   issue(0);
   for (int c = 0; c < nchunks; ++c) {
     // chunk c's loads were issued before chunk c-1's four score stores
@@ -217,93 +197,30 @@ __global__ __launch_bounds__(512) void attn_scores(const float* __restrict__ Q, 
       f32x4 s = sh[kt];
       if constexpr (CHAINS == 2) s = s + sl[kt];
       *reinterpret_cast<f32x4*>(srow + c * cstride + 16 * kt) = s;
+      mrun = fmaxf(mrun, fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
     }
   }
-}
-
-// Step 2, one workgroup per row (chunk-blocked layout; n <= 32768): the row is
-// read once into registers, P~ written back in place, m and l written per row.
-// Thread t holds the values at columns 4 (512 i + t) .. +3; the row sum adds
-// each thread's values in order, then the threads' partial sums.
-__global__ __launch_bounds__(kSoftmaxThreads) void softmax_rows_regs(float* __restrict__ S, int nq, int n,
-                                                                   float* __restrict__ m_out,
-                                                                   float* __restrict__ l_out) {
-  __shared__ float red[kSoftmaxThreads / 64];
-  const int q = blockIdx.x;
-  f32x4 v[kSoftmaxVec];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kSoftmaxVec; ++i) {
-    const int c = (i * kSoftmaxThreads + threadIdx.x) * 4;
-    if (c < n) {
-      v[i] = *reinterpret_cast<const f32x4*>(S + blk_index(nq, q, c));
-      mx = fmaxf(mx, fmaxf(fmaxf(v[i][0], v[i][1]), fmaxf(v[i][2], v[i][3])));
-    }
-  }
-  mx = block_reduce<true>(mx, red);
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < kSoftmaxVec; ++i) {
-    const int c = (i * kSoftmaxThreads + threadIdx.x) * 4;
-    if (c < n) {
-      f32x4 p;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = __builtin_amdgcn_exp2f((v[i][e] - mx) * kLog2e);
-        sum += p[e];
-      }
-      *reinterpret_cast<f32x4*>(S + blk_index(nq, q, c)) = p;
-    }
-  }
-  sum = block_reduce<false>(sum, red);
-  if (threadIdx.x == 0) {
-    m_out[q] = mx;
-    l_out[q] = sum;
-  }
-}
-
-// Rows longer than the register budget: one pass for the max, one for P~ and l.
-__global__ __launch_bounds__(kSoftmaxThreads) void softmax_rows_2pass(float* __restrict__ S, int nq, int64_t n,
-                                                                    float* __restrict__ m_out,
-                                                                    float* __restrict__ l_out) {
-  __shared__ float red[kSoftmaxThreads / 64];
-  const int q = blockIdx.x;
-  float mx = -INFINITY;
-  for (int64_t c = threadIdx.x * 4; c < n; c += kSoftmaxThreads * 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(S + blk_index(nq, q, c));
-    mx = fmaxf(mx, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-  }
-  mx = block_reduce<true>(mx, red);
-  float sum = 0.f;
-  for (int64_t c = threadIdx.x * 4; c < n; c += kSoftmaxThreads * 4) {
-    f32x4* p = reinterpret_cast<f32x4*>(S + blk_index(nq, q, c));
-    f32x4 x = *p;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = __builtin_amdgcn_exp2f((x[e] - mx) * kLog2e);
-      sum += x[e];
-    }
-    *p = x;
-  }
-  sum = block_reduce<false>(sum, red);
-  if (threadIdx.x == 0) {
-    m_out[q] = mx;
-    l_out[q] = sum;
-  }
+  // the four lanes lr + 16 g hold the slice's keys of one query
+  mrun = fmaxf(mrun, __shfl_xor(mrun, 16, 64));
+  mrun = fmaxf(mrun, __shfl_xor(mrun, 32, 64));
+  if (g == 0) Ms[(int64_t)sp * nq + qw + lr] = mrun;
 }
 
 // Step 3 for 128 queries and one key slice: O_s^T (128 dims x 16 queries per
-// wave) += V16T . P~^T, the P~ fragments split into f16 hi (one chain) and lo
-// (a second chain, CHAINS == 2, or the same one).  Per 64-key chunk a stage
-// holds the V16T tile (128 dim rows of 64 keys, 128-byte rows swizzled like a
-// GEMM operand tile) and the chunk's P~ block (128 query rows of 64 fp32,
-// 256-byte rows whose 16-byte chunks are XOR-swizzled by row % 16, so that the
-// 16 rows one fragment read touches fall on distinct banks).  Three stages
-// of direct-to-LDS loads keep two chunks in flight.
+// wave) += V16T . P~^T, the P~ fragments formed from the scores and the row
+// maximum m = max over slices of Ms (p_tilde) and split into f16 hi (one chain)
+// and lo (a second chain, CHAINS == 2, or the same one); the slice's row sums
+// of P~ go to Ls[slice][q].  Per 64-key chunk a stage holds the V16T tile
+// (128 dim rows of 64 keys, 128-byte rows swizzled like a GEMM operand tile)
+// and the chunk's S block (128 query rows of 64 fp32, 256-byte rows whose
+// 16-byte chunks are XOR-swizzled by row % 16, so that the 16 rows one
+// fragment read touches fall on distinct banks).  Three stages of
+// direct-to-LDS loads keep two chunks in flight.
 template <int CHAINS>
-__global__ __launch_bounds__(512) void attn_pv(const float* __restrict__ P, const uint16_t* __restrict__ VqT,
-                                               float* __restrict__ Opart, int nq, int64_t nk, int kps, int qblocks,
-                                               int xcd_map) {
+__global__ __launch_bounds__(512) void attn_pv(const float* __restrict__ S, const float* __restrict__ Ms,
+                                               const uint16_t* __restrict__ VqT, float* __restrict__ Opart,
+                                               float* __restrict__ Ls, int nq, int64_t nk, int kps, int splits,
+                                               int qblocks, int xcd_map) {
   constexpr int BK = 64, NST = 3, VST = kAttnD * BK, PST = kAttnQ * kAttnKV * 2;  // 16-bit elements
   constexpr int STAGE = VST + PST, NW = 8, VL = 2, PL = 4, PER = VL + PL;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[NST * STAGE];
@@ -335,7 +252,7 @@ __global__ __launch_bounds__(512) void attn_pv(const float* __restrict__ P, cons
 #pragma unroll
     for (int i = 0; i < VL; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(base + (wave + NW * i) * 512), 16, voff[i], 0, 0, 0);
-    const rsrc_t rp = make_rsrc(P + ((key0 >> 6) * nq + qb * kAttnQ) * kAttnKV, PST * 2);
+    const rsrc_t rp = make_rsrc(S + ((key0 >> 6) * nq + qb * kAttnQ) * kAttnKV, PST * 2);
 #pragma unroll
     for (int i = 0; i < PL; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_ptr_t)(base + VST + (wave + NW * i) * 512), 16, poff[i], 0, 0,
@@ -349,6 +266,15 @@ __global__ __launch_bounds__(512) void attn_pv(const float* __restrict__ P, cons
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int h = 0; h < 2; ++h) pcol[t][h] = (wave * 16 + lr) * 128 + (((8 * t + 2 * g + h) ^ lr) << 3);
+  // m of the lane's query row: the maximum of the slices' maxima.  The empty
+  // asm consumes it here, so the wait for these loads comes before the first
+  // stage's loads are issued; a first use inside the chunk loop would wait for
+  // every load in flight at each chunk.
+  const int row = qb * kAttnQ + wave * 16 + lr;
+  float mq = -INFINITY;
+  for (int s2 = 0; s2 < splits; ++s2) mq = fmaxf(mq, Ms[(int64_t)s2 * nq + row]);
+  asm volatile("" : "+v"(mq));
+  float lsum = 0.f;  // the lane's P~ values of this slice: per-chunk sums, added in chunk order
   f32x4 oh[8], ol[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -368,15 +294,26 @@ __global__ __launch_bounds__(512) void attn_pv(const float* __restrict__ P, cons
     const uint16_t* sv = lds + (c % NST) * STAGE;
     const uint16_t* spp = sv + VST;
     u32x4 ph[2], pl[2];
+    float csum = 0.f;  // the lane's 16 P~ values of the chunk, in key order
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const f32x4 x0 = __builtin_bit_cast(f32x4, lds_read16(spp, pcol[t][0]));
-      const f32x4 x1 = __builtin_bit_cast(f32x4, lds_read16(spp, pcol[t][1]));
+      f32x4 x0 = __builtin_bit_cast(f32x4, lds_read16(spp, pcol[t][0]));
+      f32x4 x1 = __builtin_bit_cast(f32x4, lds_read16(spp, pcol[t][1]));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x0[e] = p_tilde(x0[e], mq);
+        x1[e] = p_tilde(x1[e], mq);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) csum += x0[e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) csum += x1[e];
       const Split2 a = split2(x0[0], x0[1]), b = split2(x0[2], x0[3]);
       const Split2 e = split2(x1[0], x1[1]), f = split2(x1[2], x1[3]);
       ph[t] = u32x4{a.hi, b.hi, e.hi, f.hi};
       pl[t] = u32x4{a.lo, b.lo, e.lo, f.lo};
     }
+    lsum += csum;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -387,8 +324,12 @@ __global__ __launch_bounds__(512) void attn_pv(const float* __restrict__ P, cons
         corr = mfma<0, MFL_F16>(a, pl[t], corr);
       }
   }
+  // l of the slice: the four lanes lr + 16 g hold its keys of one query
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (g == 0) Ls[(int64_t)sp * nq + row] = lsum;
   // lane holds O_s^T dims 16 i + 4 g .. +3 of query qb*128 + wave*16 + lr
-  float* orow = Opart + ((int64_t)sp * nq + qb * kAttnQ + wave * 16 + lr) * kAttnD;
+  float* orow = Opart + ((int64_t)sp * nq + row) * kAttnD;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     f32x4 o = oh[i];
@@ -397,14 +338,20 @@ __global__ __launch_bounds__(512) void attn_pv(const float* __restrict__ P, cons
   }
 }
 
-// Step 4: O[r][c..c+3] = (sum over slices s = 0, 1, ... of part[s][r][c..]) / l[r].
-__global__ __launch_bounds__(256) void reduce_slices(const float* __restrict__ part, int splits, int64_t stride,
-                                                   const float* __restrict__ l, float* __restrict__ O, int64_t total4) {
+// Step 4: O[r][c..c+3] = (sum over slices s = 0, 1, ... of part[s][r][c..]) / l[r],
+// with l[r] = sum over slices s = 0, 1, ... of Ls[s][r].
+__global__ __launch_bounds__(256) void reduce_slices(const float* __restrict__ part, int splits, int nq,
+                                                   const float* __restrict__ Ls, float* __restrict__ O, int64_t total4) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // f32x4 index
   if (i >= total4) return;
+  const int64_t r = i / (kAttnD / 4), stride = (int64_t)nq * kAttnD;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) acc += reinterpret_cast<const f32x4*>(part + s * stride)[i];
-  reinterpret_cast<f32x4*>(O)[i] = acc / l[i / (kAttnD / 4)];
+  float l = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    acc += reinterpret_cast<const f32x4*>(part + s * stride)[i];
+    l += Ls[(int64_t)s * nq + r];
+  }
+  reinterpret_cast<f32x4*>(O)[i] = acc / l;
 }
 
 struct Workspace {
@@ -430,10 +377,10 @@ Workspace plan(int64_t nq, int64_t nk, int64_t d) {
   int64_t off = 0;
   w.s_off = off;
   off = align256(off + nq * nk * 4);
-  w.m_off = off;
-  off = align256(off + nq * 4);
-  w.l_off = off;
-  off = align256(off + nq * 4);
+  w.m_off = off;  // per slice and query: the slice's maximum score
+  off = align256(off + (int64_t)w.splits * nq * 4);
+  w.l_off = off;  // per slice and query: the slice's sum of P~
+  off = align256(off + (int64_t)w.splits * nq * 4);
   w.part_off = off;
   off = align256(off + (int64_t)w.splits * nq * d * 4);
   w.k16_off = off;
@@ -492,28 +439,25 @@ int attention_launch(int64_t nq, int64_t nk, int64_t d, const float* q, const fl
   const int NQ = (int)nq, qblocks = (int)(nq / kAttnQ), nwg = qblocks * w.splits, xcd_map = nwg % 8 == 0;
   int st;
   hipLaunchKernelGGL(attn_prep_kvt, dim3((unsigned)(nk / kAttnKV)), dim3(512), 0, s, k, v, k16, vt, nk);
-  // 1. S = split(Q) . round(K)^T, chunk-blocked
+  // 1. S = split(Q) . round(K)^T, chunk-blocked; each slice's row maxima
   if (chains == 2)
-    hipLaunchKernelGGL(attn_scores<2>, dim3(nwg), dim3(512), 0, s, q, k16, S, NQ, nk, w.kps, qblocks, xcd_map);
+    hipLaunchKernelGGL(attn_scores<2>, dim3(nwg), dim3(512), 0, s, q, k16, S, m, NQ, nk, w.kps, qblocks, xcd_map);
   else
-    hipLaunchKernelGGL(attn_scores<1>, dim3(nwg), dim3(512), 0, s, q, k16, S, NQ, nk, w.kps, qblocks, xcd_map);
+    hipLaunchKernelGGL(attn_scores<1>, dim3(nwg), dim3(512), 0, s, q, k16, S, m, NQ, nk, w.kps, qblocks, xcd_map);
   if ((st = launch_status()) != MFL_OK) return st;
-  // 2. row softmax pieces, P~ in place.
-  if (nk <= (int64_t)kSoftmaxThreads * kSoftmaxVec * 4)
-    hipLaunchKernelGGL(softmax_rows_regs, dim3(NQ), dim3(kSoftmaxThreads), 0, s, S, NQ, (int)nk, m, l);
-  else
-    hipLaunchKernelGGL(softmax_rows_2pass, dim3(NQ), dim3(kSoftmaxThreads), 0, s, S, NQ, nk, m, l);
-  if ((st = launch_status()) != MFL_OK) return st;
-  // 3. partial O per key slice: split(P~) . round(V)
+  // 2 and 3. per key slice: the row maximum over all slices, P~ formed from S
+  // as it is loaded, split(P~) . round(V) and the slice's row sums of P~
   if (chains == 2)
-    hipLaunchKernelGGL(attn_pv<2>, dim3(nwg), dim3(512), 0, s, S, vt, part, NQ, nk, w.kps, qblocks, xcd_map);
+    hipLaunchKernelGGL(attn_pv<2>, dim3(nwg), dim3(512), 0, s, S, m, vt, part, l, NQ, nk, w.kps, w.splits, qblocks,
+                       xcd_map);
   else
-    hipLaunchKernelGGL(attn_pv<1>, dim3(nwg), dim3(512), 0, s, S, vt, part, NQ, nk, w.kps, qblocks, xcd_map);
+    hipLaunchKernelGGL(attn_pv<1>, dim3(nwg), dim3(512), 0, s, S, m, vt, part, l, NQ, nk, w.kps, w.splits, qblocks,
+                       xcd_map);
   if ((st = launch_status()) != MFL_OK) return st;
   // 4. fixed-order sum of the slices, then divide by l.
   const int64_t total4 = nq * d / 4;
-  hipLaunchKernelGGL(reduce_slices, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0, s, part, w.splits, nq * d, l,
-                     o, total4);
+  hipLaunchKernelGGL(reduce_slices, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0, s, part, w.splits, NQ, l, o,
+                     total4);
   return launch_status();
 }
 
