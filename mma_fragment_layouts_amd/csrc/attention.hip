@@ -110,7 +110,7 @@ __device__ __forceinline__ int slice_chunks(int sp, int kps, int64_t nk) {
 // keeps the running maximum of its queries' scores, written per query and
 // slice at the end (Ms[slice][q]).  K16 chunks arrive by direct-to-LDS loads,
 // two stages.
-template <int CHAINS>
+template <int CHAINS, bool NT>
 __global__ __launch_bounds__(512) void attn_scores(const float* __restrict__ Q, const uint16_t* __restrict__ Kq,
                                                    float* __restrict__ S, float* __restrict__ Ms, int nq, int64_t nk,
                                                    int kps, int qblocks, int xcd_map) {
@@ -196,7 +196,10 @@ __global__ __launch_bounds__(512) void attn_scores(const float* __restrict__ Q, 
     for (int kt = 0; kt < 4; ++kt) {
       f32x4 s = sh[kt];
       if constexpr (CHAINS == 2) s = s + sl[kt];
-      *reinterpret_cast<f32x4*>(srow + c * cstride + 16 * kt) = s;
+      if constexpr (NT)
+        __builtin_nontemporal_store(s, reinterpret_cast<f32x4*>(srow + c * cstride + 16 * kt));
+      else
+        *reinterpret_cast<f32x4*>(srow + c * cstride + 16 * kt) = s;
       mrun = fmaxf(mrun, fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
     }
   }
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(512) void attn_scores(const float* __restrict__ Q, 
 // 16-byte chunks are XOR-swizzled by row % 16, so that the 16 rows one
 // fragment read touches fall on distinct banks).  Three stages of
 // direct-to-LDS loads keep two chunks in flight.
-template <int CHAINS>
+template <int CHAINS, bool NT>
 __global__ __launch_bounds__(512) void attn_pv(const float* __restrict__ S, const float* __restrict__ Ms,
                                                const uint16_t* __restrict__ VqT, float* __restrict__ Opart,
                                                float* __restrict__ Ls, int nq, int64_t nk, int kps, int splits,
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(512) void attn_pv(const float* __restrict__ S, cons
 #pragma unroll
     for (int i = 0; i < PL; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_ptr_t)(base + VST + (wave + NW * i) * 512), 16, poff[i], 0, 0,
-                                               0);
+                                               NT ? 2 : 0);  // 2: the non-temporal (streaming) policy
   };
   const FragOffsets<0, BK> fo(0, lane);  // V16T fragments: dim row 16 i + lr, keys 32 t + 8 g ..
   // P~ fragments: query row wave * 16 + lr, keys 32 t + 8 g .. +7 = logical
@@ -439,20 +442,31 @@ int attention_launch(int64_t nq, int64_t nk, int64_t d, const float* q, const fl
   const int NQ = (int)nq, qblocks = (int)(nq / kAttnQ), nwg = qblocks * w.splits, xcd_map = nwg % 8 == 0;
   int st;
   hipLaunchKernelGGL(attn_prep_kvt, dim3((unsigned)(nk / kAttnKV)), dim3(512), 0, s, k, v, k16, vt, nk);
+  // S of at least the 256 MB last-level cache (MALL) cannot stay in it between
+  // the two kernels: it is then written and read with the non-temporal policy,
+  // so that reading it does not first evict the score kernel's dirty lines.
+  const bool nt = nq * nk * 4 >= ((int64_t)256 << 20);
   // 1. S = split(Q) . round(K)^T, chunk-blocked; each slice's row maxima
-  if (chains == 2)
-    hipLaunchKernelGGL(attn_scores<2>, dim3(nwg), dim3(512), 0, s, q, k16, S, m, NQ, nk, w.kps, qblocks, xcd_map);
-  else
-    hipLaunchKernelGGL(attn_scores<1>, dim3(nwg), dim3(512), 0, s, q, k16, S, m, NQ, nk, w.kps, qblocks, xcd_map);
+#define MFL_SCORES(C, NT) \
+  hipLaunchKernelGGL((attn_scores<C, NT>), dim3(nwg), dim3(512), 0, s, q, k16, S, m, NQ, nk, w.kps, qblocks, xcd_map)
+  if (chains == 2) {
+    if (nt) MFL_SCORES(2, true); else MFL_SCORES(2, false);
+  } else {
+    if (nt) MFL_SCORES(1, true); else MFL_SCORES(1, false);
+  }
+#undef MFL_SCORES
   if ((st = launch_status()) != MFL_OK) return st;
   // 2 and 3. per key slice: the row maximum over all slices, P~ formed from S
   // as it is loaded, split(P~) . round(V) and the slice's row sums of P~
-  if (chains == 2)
-    hipLaunchKernelGGL(attn_pv<2>, dim3(nwg), dim3(512), 0, s, S, m, vt, part, l, NQ, nk, w.kps, w.splits, qblocks,
-                       xcd_map);
-  else
-    hipLaunchKernelGGL(attn_pv<1>, dim3(nwg), dim3(512), 0, s, S, m, vt, part, l, NQ, nk, w.kps, w.splits, qblocks,
-                       xcd_map);
+#define MFL_PV(C, NT)                                                                                            \
+  hipLaunchKernelGGL((attn_pv<C, NT>), dim3(nwg), dim3(512), 0, s, S, m, vt, part, l, NQ, nk, w.kps, w.splits, \
+                     qblocks, xcd_map)
+  if (chains == 2) {
+    if (nt) MFL_PV(2, true); else MFL_PV(2, false);
+  } else {
+    if (nt) MFL_PV(1, true); else MFL_PV(1, false);
+  }
+#undef MFL_PV
   if ((st = launch_status()) != MFL_OK) return st;
   // 4. fixed-order sum of the slices, then divide by l.
   const int64_t total4 = nq * d / 4;
