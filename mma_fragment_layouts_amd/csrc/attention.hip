@@ -350,6 +350,9 @@ __global__ __launch_bounds__(256) void reduce_slices(const float* __restrict__ p
   const int64_t r = i / (kAttnD / 4), stride = (int64_t)nq * kAttnD;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
+  // unrolled so that the loads of several slices are in flight together; the
+  // sums still run in slice order
+#pragma unroll 8
   for (int s = 0; s < splits; ++s) {
     acc += reinterpret_cast<const f32x4*>(part + s * stride)[i];
     l += Ls[(int64_t)s * nq + r];
