@@ -109,21 +109,25 @@ def test_split_gemm_random_shape(case):
     assert acc_err <= (2e-6 if chains >= 2 else 2e-5)
 
 
-def attention_cases(count=12, seed=5):
+def attention_cases(count=40, seed=5):
+    """(nq, nk, chains, algo, q scale): up to 1,024 queries and 20,480 keys; Q
+    scaled by 1, 4 or 16 moves the scores from about 1 to about 16 in size, so
+    that the softmax references move more often."""
     rng = np.random.default_rng(seed)
-    return [(128 * int(rng.integers(1, 9)), 128 * int(rng.integers(1, 65)), int(rng.integers(1, 3)), int(rng.integers(0, 3)))
-            for _ in range(count)]
+    return [(128 * int(rng.integers(1, 9)), 128 * int(rng.integers(1, 161)), int(rng.integers(1, 3)),
+             int(rng.integers(0, 3)), int(rng.choice([1, 4, 16]))) for _ in range(count)]
 
 
-@pytest.mark.parametrize("case", attention_cases(), ids=lambda c: f"{c[0]}x{c[1]}-ch{c[2]}-algo{c[3]}")
+@pytest.mark.parametrize("case", attention_cases(), ids=lambda c: f"{c[0]}x{c[1]}-ch{c[2]}-algo{c[3]}-q{c[4]}")
 def test_attention_random_shape(case):
     """Random query and key counts (multiples of 128) through every attention
     algorithm: key-slice counts and per-slice chunk counts vary, odd ones
     included; against the fp64 oracle (on the quantisation each algorithm
     applies: K and V rounded once, or split too for algorithm 2)."""
-    nq, nk, chains, algo = case
+    nq, nk, chains, algo, qscale = case
     say("random attention", case)
     q, k, v = inputs.attention(nq, nk)
+    q = q * np.float32(qscale)
     wsb = mfl.attention_workspace_bytes(nq, nk, 128, algo)
     ws = torch.empty(wsb, dtype=torch.uint8, device=device())
     o = torch.full((nq, 128), np.nan, device=device())
