@@ -160,8 +160,16 @@ __global__ __launch_bounds__(512) void attn_scores(const float* __restrict__ Q, 
     asm volatile("" ::: "memory");  // the loads stay ahead of the chunk's score stores
   };
   const FragOffsets<0, BK> fo(0, lane);
-  // lane's keys 16 kt + 4 g .. +3 of each chunk, query qw + lr
-  float* srow = S + ((kbeg >> 6) * nq + qw + lr) * kAttnKV + 4 * g;
+  // The lane holds keys 16 kt + 4 g .. +3 of each chunk for query qw + lr and
+  // stores them as 16 bytes (each store instruction: 64-byte pieces of 16 rows,
+  // which the L2 merges into lines).  Non-temporal stores (NT) bypass that
+  // merge and would move each piece as a line of its own, so there the wave's
+  // 16 x 64 tile goes through a wave-private LDS tile (rows padded to 68
+  // floats) and each store instruction writes four whole 256-byte rows.
+  __shared__ __attribute__((aligned(16))) float stg[NT ? NW : 1][16][68];
+  float (*tile)[68] = stg[NT ? wave : 0];
+  float* sblk = S + (kbeg >> 6) * (int64_t)nq * kAttnKV + (int64_t)qw * kAttnKV;
+  float* srow = sblk + lr * kAttnKV + 4 * g;
   const int64_t cstride = (int64_t)nq * kAttnKV;
   float mrun = -INFINITY;  // maximum of the lane's scores of query qw + lr
   issue(0);
@@ -197,10 +205,22 @@ __global__ __launch_bounds__(512) void attn_scores(const float* __restrict__ Q, 
       f32x4 s = sh[kt];
       if constexpr (CHAINS == 2) s = s + sl[kt];
       if constexpr (NT)
-        __builtin_nontemporal_store(s, reinterpret_cast<f32x4*>(srow + c * cstride + 16 * kt));
+        *reinterpret_cast<f32x4*>(&tile[lr][16 * kt + 4 * g]) = s;
       else
         *reinterpret_cast<f32x4*>(srow + c * cstride + 16 * kt) = s;
       mrun = fmaxf(mrun, fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+    }
+    if constexpr (NT) {
+      // LDS operations of one wave complete in order: the reads below see the
+      // writes above (the asm keeps the compiler from reordering them)
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * i + (lane >> 4), col = 4 * (lane & 15);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&tile[row][col]);
+        __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(sblk + c * cstride + row * kAttnKV + col));
+      }
+      asm volatile("" ::: "memory");  // the tile's reads stay before the next chunk's writes
     }
   }
   // the four lanes lr + 16 g hold the slice's keys of one query
