@@ -289,14 +289,15 @@ __global__ __launch_bounds__(512) void attn_pv(const float* __restrict__ S, cons
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int h = 0; h < 2; ++h) pcol[t][h] = (wave * 16 + lr) * 128 + (((8 * t + 2 * g + h) ^ lr) << 3);
-  // m of the lane's query row: the maximum of the slices' maxima.  The empty
-  // asm consumes it here, so the wait for these loads comes before the first
-  // stage's loads are issued; a first use inside the chunk loop would wait for
-  // every load in flight at each chunk.
+  // m of the lane's query row: the maximum of the slices' maxima, loaded 16
+  // slices at a time (one load per iteration would wait out each latency in
+  // turn).  An empty asm consumes m once the first stages' loads are issued
+  // (below), so its wait overlaps them; a first use inside the chunk loop would
+  // wait for every load in flight at each chunk.
   const int row = qb * kAttnQ + wave * 16 + lr;
   float mq = -INFINITY;
+#pragma unroll 16
   for (int s2 = 0; s2 < splits; ++s2) mq = fmaxf(mq, Ms[(int64_t)s2 * nq + row]);
-  asm volatile("" : "+v"(mq));
   float lsum = 0.f;  // the lane's P~ values of this slice: per-chunk sums, added in chunk order
   f32x4 oh[8], ol[8];
 #pragma unroll
@@ -307,6 +308,7 @@ __global__ __launch_bounds__(512) void attn_pv(const float* __restrict__ S, cons
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < nchunks) fetch(s);
+  asm volatile("" : "+v"(mq));
   for (int c = 0; c < nchunks; ++c) {
     if (c + NST - 2 < nchunks)
       wait_vmcnt<(NST - 2) * PER>();
